@@ -1,0 +1,76 @@
+"""Algorithmic work and traffic of attention, for throughput and rooflines.
+
+FLOPs count what the method must compute, with the real head dimension d:
+
+* forward: 4 * B * Hq * Nq * Nk * d (two matrix products of 2*N*N*d each),
+  halved for causal attention -- the 4N^2 d count of page
+  "FlashAttention技术解析：优化Transformer注意力计算效率"
+  (jsqmd.com/news/722897) §3.1;
+* backward: 10 * B * Hq * Nq * Nk * d (recompute of S plus dV, dP, dQ, dK),
+  halved for causal.
+
+Bytes are the minimum traffic: Q, K, V (and the optional lengths) read once,
+O and LSE written once.  K/V re-reads, padding and recompute are not counted.
+"""
+from __future__ import annotations
+
+ELEM_BYTES = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+# MI355X published peaks
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def fwd_flops(B, Hq, Nq, Nk, d, causal=False) -> float:
+    f = 4.0 * B * Hq * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def bwd_flops(B, Hq, Nq, Nk, d, causal=False) -> float:
+    f = 10.0 * B * Hq * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def useful_pairs(Nq, Nk, kv_lens=None, causal=False, B=1) -> int:
+    """Number of visible (query, key) pairs summed over the batch."""
+    lens = [Nk] * B if kv_lens is None else [min(max(int(x), 0), Nk) for x in kv_lens]
+    tot = 0
+    for L in lens:
+        if causal:
+            # query i sees keys 0..min(i, L-1)
+            full = min(L, Nq)
+            tot += full * (full + 1) // 2 + max(Nq - L, 0) * L
+        else:
+            tot += Nq * L
+    return tot
+
+
+def fwd_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, with_lens=False) -> int:
+    e = ELEM_BYTES[dtype]
+    return (B * Hq * Nq * d * e * 2          # Q in, O out
+            + B * Hkv * Nk * d * e * 2       # K, V in
+            + B * Hq * Nq * 4                # LSE out
+            + (B * 4 if with_lens else 0))
+
+
+def bwd_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, grad_bytes=4) -> int:
+    e = ELEM_BYTES[dtype]
+    return (B * Hq * Nq * d * e * 3          # Q, O, dO in
+            + B * Hkv * Nk * d * e * 2       # K, V in
+            + B * Hq * Nq * 4 * 2            # LSE in, D out/in
+            + B * Hq * Nq * d * grad_bytes   # dQ out
+            + B * Hkv * Nk * d * grad_bytes * 2)  # dK, dV out
+
+
+def score_matrix_bytes(B, H, N, elem_bytes=4) -> int:
+    """Size of a materialised [B, H, N, N] score matrix."""
+    return B * H * N * N * elem_bytes
+
+
+def unfused_io_elements(N, d) -> int:
+    """HBM elements moved by the unfused three-step chain for one head.
+
+    Step 1 reads Q, K (2Nd) and writes S (N^2); step 2 reads S and writes P
+    (2N^2); step 3 reads P and V (N^2 + Nd) and writes O (Nd): 4N^2 + 4Nd.
+    """
+    return 4 * N * N + 4 * N * d
