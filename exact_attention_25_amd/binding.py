@@ -1,0 +1,208 @@
+"""Thin ctypes binding over the C ABI of ``libattn.so`` (``include/attn.h``).
+
+Argument marshalling only: the functions here check tensor shapes, allocate
+outputs with torch (the library itself never allocates), pass raw device
+pointers and the current HIP stream, and turn a non-OK status into an
+exception.  Every step of the computation runs in the library's kernels;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EALIGN, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
+ATTN_FP32, ATTN_FP16, ATTN_BF16 = 0, 1, 2
+ATTN_BHND, ATTN_BNHD = 0, 1
+
+EXPORTS = ("attn_validate", "attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd",
+           "attn_status_string")
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Nq", ctypes.c_int32), ("Nk", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("mask", ctypes.c_void_p),
+        ("mask_sb", ctypes.c_int64), ("mask_sh", ctypes.c_int64), ("mask_sq", ctypes.c_int64),
+        ("kv_lens", ctypes.c_void_p),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load the library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(AttnParams)
+    vp = ctypes.c_void_p
+    lib.attn_validate.argtypes = [P, ctypes.c_int]
+    lib.attn_validate.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [P]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                             ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def make_params(B, Hq, Hkv, Nq, Nk, d, dtype=ATTN_BF16, layout=ATTN_BHND, scale=None,
+                causal=False, mask_ptr=None, mask_strides=(0, 0, 0), kv_lens_ptr=None) -> AttnParams:
+    p = AttnParams()
+    p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = B, Hq, Hkv, Nq, Nk, d
+    p.dtype, p.layout = dtype, layout
+    p.scale = 0.0 if scale is None else float(scale)
+    p.causal = 1 if causal else 0
+    p.mask = mask_ptr
+    p.mask_sb, p.mask_sh, p.mask_sq = (int(x) for x in mask_strides)
+    p.kv_lens = kv_lens_ptr
+    return p
+
+
+def attn_validate(params: AttnParams, for_backward: bool = False) -> int:
+    return load().attn_validate(ctypes.byref(params), 1 if for_backward else 0)
+
+
+def attn_bwd_workspace_bytes(params: AttnParams) -> int:
+    return int(load().attn_bwd_workspace_bytes(ctypes.byref(params)))
+
+
+# ----------------------------------------------------------------- torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: ATTN_FP32, torch.float16: ATTN_FP16, torch.bfloat16: ATTN_BF16}[t]
+
+
+def _layout_code(layout: str) -> int:
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
+    return ATTN_BHND if layout == "bhnd" else ATTN_BNHD
+
+
+def _dims(q, k, v, layout):
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v must be 4-D and k, v must have the same shape")
+    if layout == "bhnd":
+        B, Hq, Nq, d = q.shape
+        Bk, Hkv, Nk, dk = k.shape
+    else:
+        B, Nq, Hq, d = q.shape
+        Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def attn_fwd(q, k, v, *, layout="bhnd", causal=False, scale=None, attn_mask=None,
+             kv_lens=None, out=None, lse=None):
+    """Forward attention.  Returns (o, lse).
+
+    q: [B,Hq,Nq,d] ("bhnd") or [B,Nq,Hq,d] ("bnhd"); k, v likewise with Hkv
+    heads.  attn_mask: optional float32 tensor broadcastable to [B,Hq,Nq,Nk]
+    (additive, logit units).  kv_lens: optional int32 [B] device tensor.
+    """
+    torch = _torch()
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
+    mask_ptr, mstr = None, (0, 0, 0)
+    if attn_mask is not None:
+        if attn_mask.dtype != torch.float32 or not attn_mask.is_cuda:
+            raise ValueError("attn_mask must be a float32 device tensor")
+        m = attn_mask.expand(B, Hq, Nq, Nk)
+        if m.stride(3) != 1:
+            m = m.contiguous()
+        attn_mask = m
+        mask_ptr, mstr = m.data_ptr(), (m.stride(0), m.stride(1), m.stride(2))
+    lens_ptr = None
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
+            raise ValueError("kv_lens must be an int32 device tensor with B entries")
+        kv_lens = kv_lens.contiguous()
+        lens_ptr = kv_lens.data_ptr()
+    p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
+                    causal, mask_ptr, mstr, lens_ptr)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib.attn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr(), _stream_ptr(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, kv_lens=None,
+             grad_dtype="fp32", workspace=None):
+    """Backward attention from the forward's (o, lse).  Returns (dq, dk, dv)."""
+    torch = _torch()
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
+    if dout.shape != q.shape or o.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    lens_ptr = None
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
+            raise ValueError("kv_lens must be an int32 device tensor with B entries")
+        kv_lens = kv_lens.contiguous()
+        lens_ptr = kv_lens.data_ptr()
+    p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
+                    causal, None, (0, 0, 0), lens_ptr)
+    gcode = ATTN_FP32 if grad_dtype == "fp32" else _dtype_code(q.dtype)
+    gdt = torch.float32 if gcode == ATTN_FP32 else q.dtype
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device)
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device)
+    dv = torch.empty(v.shape, dtype=gdt, device=q.device)
+    need = attn_bwd_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), dout.contiguous().data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                      dv.data_ptr(), gcode, workspace.data_ptr(), workspace.numel(),
+                      _stream_ptr(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI host code and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Kernel arguments of the forward pass.  Strides are in elements; d is the
+// contiguous dimension of every tensor.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* mask;
+  const int32_t* kv_lens;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t m_sb, m_sh, m_sq;
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t group;         // Hq / Hkv
+  int32_t nqb;           // query blocks per head (set by the launcher)
+  int32_t total_blocks;  // B * Hq * nqb (set by the launcher)
+  float c;               // scale * log2(e)
+};
+
+// Kernel arguments of the backward pass (16-bit inputs).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;          // [B, Hq, Nq] workspace: rowsum(dout * o)
+  const int32_t* kv_lens;
+  int64_t q_sb, q_sh, q_sn;   // q, o, dout, dq share these
+  int64_t k_sb, k_sh, k_sn;   // k, v, dk, dv share these
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t group;
+  float scale;           // softmax scale
+  float c;               // scale * log2(e)
+  int32_t grad_f32;      // 1: dq/dk/dv are fp32, 0: input dtype
+};
+
+hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, bool causal, bool mask, hipStream_t st);
+hipError_t launch_fwd32(const FwdArgs& a, bool causal, bool mask, hipStream_t st);
+hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, bool causal, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,129 @@
+// Device-side helpers shared by the forward and backward kernels (gfx950).
+//
+// Lane layouts used throughout (wave64, measured on gfx950):
+//   v_mfma_f32_32x32x16_{bf16,f16}:
+//     A (32 x 16): lane l holds row l%32, k = (l/32)*8 + 0..7   (8 x 16-bit)
+//     B (16 x 32): lane l holds col l%32, k = (l/32)*8 + 0..7
+//     D (32 x 32): lane l holds col l%32, register r holds row
+//                  (r/4)*8 + (l/32)*4 + r%4                     (16 x fp32)
+//   v_mfma_f32_32x32x2_f32: as above with k = l/32 (one fp32 per lane).
+//   ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives as
+//     element j the (l%4)-th 16-bit value of the 8 bytes that lane 4j + l/4
+//     of the group addressed.  Lane i pointing at row r0 + i/4, column
+//     c0 + 4*(i%4) of a row-major tile therefore gives lane l the column
+//     c0 + l of rows r0..r0+3: a transposed read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-bit element traits: storage type, 8-wide operand vector, MFMA, rounding.
+struct BF16 {
+  using T = __bf16;
+  using V8 = bf16x8;
+  using V4 = bf16x4;
+  using V2 = bf16x2;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ V2 cvt2(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_convertvector(v, V2);
+  }
+};
+
+struct FP16 {
+  using T = _Float16;
+  using V8 = f16x8;
+  using V4 = f16x4;
+  using V2 = f16x2;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ V2 cvt2(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_convertvector(v, V2);
+  }
+};
+
+template <class V8, class V4>
+__device__ __forceinline__ V8 concat4(V4 lo, V4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposed 8-byte LDS read (see the layout note above).
+template <class V4>
+__device__ __forceinline__ V4 lds_read_tr4(const char* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(LDS_AS void*)(p));
+  return __builtin_bit_cast(V4, r);
+}
+
+template <class V8>
+__device__ __forceinline__ V8 lds_read16(const char* p) {
+  return *(const LDS_AS V8*)(const LDS_AS void*)(p);
+}
+
+// One 16-byte global -> LDS copy per lane.  Lane i of the wave writes the
+// 16 bytes at lds_wave_base + 16 * i; lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* gsrc, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (LDS_AS void*)lds_wave_base, 16, 0, 0);
+}
+
+// Value of x held by lane l ^ 32, combined with x by max / add.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Work-group ids are handed to the 8 XCDs round-robin (id % 8).  Remap so
+// that consecutive logical ids -- the query blocks of one head -- run on the
+// same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int hw_id, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = hw_id % 8, idx = hw_id / 8;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// LDS swizzles for a row-major tile of rows of CPR 16-byte chunks.
+// K-type tiles are read 16 rows x one chunk at a time (ds_read_b128): the XOR
+// spreads 16 consecutive rows over distinct chunk slots of a 256-byte window.
+// V-type tiles are read 4 rows x two adjacent chunks (transposed reads): the
+// XOR by an even value keeps the pair adjacent and spreads the 4 rows.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (CPR >= 16) return row & 15;
+  else return (row >> 1) & (CPR - 1);
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (CPR >= 16) return (row & 7) << 1;
+  else return ((row >> 1) & 3) << 1;
+}
+
+}  // namespace attn

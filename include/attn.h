@@ -1,0 +1,142 @@
+/*
+ * attn.h -- C ABI of the exact-attention library for MI355X (gfx950).
+ *
+ * Computes exact scaled-dot-product attention
+ *
+ *     O = softmax(Q K^T * scale + mask) V
+ *
+ * tile by tile with an online softmax (a running row maximum m and running
+ * exponential sum l), so the N x N score matrix never reaches HBM, and writes
+ * the per-row log-sum-exp LSE so that the backward pass can form the
+ * probabilities again from LSE instead of storing them.
+ *
+ * Sources (web pages, by title and section):
+ *   - the unfused chain S = QK^T, S/sqrt(d_k), S + attn_mask, softmax, S V:
+ *     "Step 3.7 Flash 的表现有点意外" (xxmr.cn/news/81028) §2.3;
+ *   - tiling into B_r x B_c blocks and the online softmax (running m and l):
+ *     "FlashAttention技术解析：优化Transformer注意力计算效率"
+ *     (jsqmd.com/news/722897) §2.2; storing only O(N) statistics and
+ *     recomputing P in the backward: same page §3.3;
+ *   - the call surfaces that fix the argument set: F.scaled_dot_product_attention
+ *     (q, k, v in [B, H, N, d], attn_mask, is_causal) and
+ *     flash_attn_func(q, k, v, softmax_scale, causal, deterministic) in
+ *     [B, N, H, d] -- "如何在ChatGLM2-6B中集成Flash-Attention2？实测性能提升与
+ *     显存优化" (jsqmd.com/news/348824) §3 steps 3 and 4.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing and frees nothing; the backward's scratch
+ *     comes in through `workspace`.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising.  Faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - Errors are returned as attn_status; the library never aborts or prints.
+ *   - The library keeps no global state; calls on different streams may run
+ *     concurrently.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,        /* invalid shape or parameter                         */
+  ATTN_EUNSUPPORTED = 2,  /* valid, but outside what the kernels implement      */
+  ATTN_EALIGN = 3,        /* a pointer is not 16-byte aligned                   */
+  ATTN_EWORKSPACE = 4,    /* backward workspace missing or too small            */
+  ATTN_EHIP = 5           /* a kernel launch failed (hipGetLastError)           */
+} attn_status;
+
+typedef enum { ATTN_FP32 = 0, ATTN_FP16 = 1, ATTN_BF16 = 2 } attn_dtype;
+
+/* d is always the contiguous (innermost) dimension. */
+typedef enum {
+  ATTN_BHND = 0,  /* [B, H, N, d]: the scaled_dot_product_attention layout      */
+  ATTN_BNHD = 1   /* [B, N, H, d]: the flash_attn_func ("bshd") layout           */
+} attn_layout;
+
+typedef struct {
+  int32_t B;       /* batch                                                     */
+  int32_t Hq;      /* query heads                                               */
+  int32_t Hkv;     /* key/value heads; Hq % Hkv == 0; q-head h reads kv-head    */
+                   /* h / (Hq / Hkv) (grouped-query attention)                  */
+  int32_t Nq;      /* query rows per head, >= 0                                 */
+  int32_t Nk;      /* key rows per head, >= 0                                   */
+  int32_t d;       /* head dimension: 8 <= d <= 128, d % 8 == 0                 */
+  attn_dtype dtype;   /* element type of q, k, v, o and dout                   */
+  attn_layout layout; /* layout of q, k, v, o, dout, dq, dk, dv; lse is always */
+                      /* a contiguous [B, Hq, Nq] float array                  */
+  float scale;     /* softmax scale; <= 0 or NaN means 1/sqrt(d) (real d)       */
+  int32_t causal;  /* non-zero: key j is visible to query i iff j <= i;         */
+                   /* requires Nq == Nk                                         */
+  /* Optional additive float mask in logit units, added after scaling:
+   *   element (b, h, i, j) is mask[b*mask_sb + h*mask_sh + i*mask_sq + j].
+   * A stride of 0 broadcasts that dimension.  -INFINITY entries exclude a key.
+   * NULL = no mask. */
+  const float* mask;
+  int64_t mask_sb, mask_sh, mask_sq;
+  /* Optional [B] int32 valid key counts: keys j >= kv_lens[b] are excluded.
+   * Values are clamped to [0, Nk].  NULL = all Nk keys are valid. */
+  const int32_t* kv_lens;
+} attn_params;
+
+/* Host-only check of *p (no GPU call).  for_backward != 0 also checks the
+ * backward's extra constraints.  Returns ATTN_OK, ATTN_EINVAL (null p, shapes
+ * out of range (B, Nq, Nk < 0; Hq, Hkv, d < 1), Hq % Hkv != 0, causal with
+ * Nq != Nk, bad enum, negative mask stride) or ATTN_EUNSUPPORTED (d outside
+ * [8, 128] or d % 8 != 0; for the backward also an additive mask, an fp32
+ * dtype, or d other than 64 or 128).  B == 0, Nq == 0 and Nk == 0 are
+ * valid: the first two make a call a no-op, the last makes every row fully
+ * masked. */
+attn_status attn_validate(const attn_params* p, int for_backward);
+
+/* Forward pass.
+ *   q:   [B, Hq, Nq, d] or [B, Nq, Hq, d] (p->layout), p->dtype
+ *   k,v: [B, Hkv, Nk, d] or [B, Nk, Hkv, d], p->dtype
+ *   o:   output, q's shape and layout, p->dtype (rounded to nearest even)
+ *   lse: output, [B, Hq, Nq] float: natural-log log-sum-exp of the scaled,
+ *        masked logits of each row; -INFINITY (and o = 0) for a row whose
+ *        keys are all excluded.
+ * q, k, v, o, lse must be 16-byte aligned.  Returns ATTN_OK once the kernel
+ * is enqueued; ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EALIGN without
+ * enqueueing anything; ATTN_EHIP if the launch failed. */
+attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
+                     const void* v, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace attn_bwd needs for *p (0 if p is invalid). */
+size_t attn_bwd_workspace_bytes(const attn_params* p);
+
+/* Backward pass: gradients of <dout, O> with O = attention(q, k, v), with the
+ * probabilities formed again from the forward's lse (FlashAttention技术解析
+ * §3.3).  With D_i = sum_c dout_ic o_ic:
+ *   dP = dout V^T, dS = P * (dP - D), dq = scale dS K,
+ *   dk = scale dS^T Q, dv = P^T dout,
+ * where dk, dv sum over the q-heads sharing a kv-head.
+ *   o, lse: the forward's outputs for the same inputs and params
+ *   dout:   q's shape, layout and dtype
+ *   dq:     q's shape and layout; dk, dv: k's shape and layout
+ *   grad_dtype: element type of dq, dk, dv: ATTN_FP32 or p->dtype
+ *   workspace: device memory of at least attn_bwd_workspace_bytes(p) bytes,
+ *              16-byte aligned; its contents on entry do not matter.
+ * The additive mask is not supported by the backward (ATTN_EUNSUPPORTED);
+ * kv_lens and causal are.  The result is deterministic: no atomics. */
+attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     attn_dtype grad_dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */
