@@ -1,0 +1,245 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+A step is one forward call (attn_fwd through the C ABI) on the
+B=8, H=32, N=4096, d=128 bf16 workload (non-causal, no mask), inputs already
+resident in HBM.  The script prints ONE JSON line with the throughput in
+TFLOP/s (4*B*H*N^2*d per call), the roofline position of the forward kernel
+(launch duration from HIP events on the launch stream), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--extras] [--no-cpu-baseline] [--copy-calibration]
+
+--extras also times the other workloads (the ViT, UNet self/cross, causal
+GQA forward and backward, and the long-context sweep) and adds them to the
+JSON line under "extras".  --copy-calibration runs a plain device copy of a
+known size (for scaling HBM byte counters under rocprofv3).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS & % of bf16 MFMA peak at B8 H32 N4096 d128"
+DEFAULT_WORKLOAD = "long_bf16_b8_h32_n4096_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_bf16_b8_h32_n4096_d128_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_25_amd", "csrc", f)
+                  for f in ("attn_fwd.hip", "device_common.h", "attn_kernels.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def upload(raw, dtype, device):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(raw)).to(device)
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def workload_inputs(w, device, with_do=False):
+    from exact_attention_25_amd import inputs
+    x = inputs.make_inputs(w, with_do=with_do)
+    t = {n: upload(x[n + "_raw"], w.dtype, device) for n in ("q", "k", "v")}
+    if with_do:
+        t["do"] = upload(x["do_raw"], w.dtype, device)
+    import torch
+    t["kv_lens"] = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).to(device)
+    return x, t
+
+
+def cpu_baseline(w, x, budget_s=15.0):
+    """The fp64 oracle on the first heads of batch 0, until ~budget_s of CPU
+    time; returns a dict in the metric's unit (TFLOP/s)."""
+    from threadpoolctl import threadpool_info
+    from exact_attention_25_amd import accounting as acc
+    from oracle import ref_fwd
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.Hq:
+        sl = slice(heads, heads + 1)
+        g = heads // (w.Hq // w.Hkv)
+        lens = None if x["kv_lens"] is None else x["kv_lens"][:1]
+        ref_fwd(x["q"][:1, sl], x["k"][:1, g:g + 1], x["v"][:1, g:g + 1], causal=w.causal,
+                kv_lens=lens)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = acc.fwd_flops(1, heads, w.Nq, w.Nk, w.d, w.causal)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle forward on {heads} of {w.B * w.Hq} heads "
+                      f"(batch 0, heads 0..{heads - 1}) of {w.name}, {dt:.1f} s"}
+
+
+def run_extras(device, steps, warmup):
+    import torch
+    from exact_attention_25_amd import accounting as acc
+    from exact_attention_25_amd import binding as bd
+    from exact_attention_25_amd import inputs
+    stream = torch.cuda.current_stream(device)
+    out = {}
+    names = ["vit_bf16_b128_h16_n196_d64", "unet_self_fp16_b2_h8_n4096_d40",
+             "unet_cross_fp16_b2_h8_q4096_k77_d40", "causal_gqa_bf16_b4_h32_kv2_n8192_d128"]
+    ws = [inputs.WORKLOADS[n] for n in names] + [inputs.sweep_workload(n) for n in
+                                                   (1024, 2048, 8192, 16384)]
+    for w in ws:
+        x, t = workload_inputs(w, device, with_do=w.backward)
+        fn = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"])
+        ms, _ = time_calls(fn, steps, warmup, stream)
+        fl = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+        by = acc.fwd_min_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.dtype, x["kv_lens"] is not None)
+        rec = {"fwd_ms": round(ms, 4), "fwd_tflops": round(fl / ms / 1e9, 1),
+               "fwd_pct_peak": round(fl / ms / 1e9 / acc.PEAK_TFLOPS[w.dtype] * 100, 2),
+               "fwd_min_bytes_gbs": round(by / ms / 1e6, 1),
+               "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1)}
+        if w.backward:
+            o, lse = fn()
+            bfn = lambda: bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal,
+                                      kv_lens=t["kv_lens"])
+            try:
+                bms, _ = time_calls(bfn, max(steps // 2, 2), 2, stream)
+                bfl = acc.bwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+                rec.update({"bwd_ms": round(bms, 4), "bwd_tflops": round(bfl / bms / 1e9, 1),
+                            "bwd_pct_peak": round(bfl / bms / 1e9 / acc.PEAK_TFLOPS[w.dtype] * 100, 2)})
+            except bd.AttnError as e:
+                rec["bwd_error"] = str(e)
+        out[w.name] = rec
+        del t
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the attention of every (batch, head) is "
+              f"independent and this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_25_amd import accounting as acc
+    from exact_attention_25_amd import binding as bd
+    from exact_attention_25_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.load()
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    stream = torch.cuda.current_stream(device)
+
+    w = inputs.WORKLOADS.get(args.workload)
+    if w is None:
+        m = re.match(r"long_bf16_sweep_b\d+_h32_n(\d+)_d128", args.workload)
+        if not m:
+            raise SystemExit(f"unknown workload {args.workload}")
+        w = inputs.sweep_workload(int(m.group(1)))
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    x, t = workload_inputs(w, device)
+
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 28, dtype=torch.float32, device=device).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 x 1 GiB device copies", file=sys.stderr, flush=True)
+        del src, dst
+
+    fn = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"])
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    ms, wall = time_calls(fn, args.steps, args.warmup, stream)
+
+    flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    tflops = flops / ms / 1e9
+    peak = acc.PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, numpy PCG64, rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "Hkv": w.Hkv, "N": w.Nq,
+                   "d": w.d, "causal": w.causal, "mask": None, "pass": "forward"},
+        "pct_of_peak": round(tflops / peak * 100, 2),
+        "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": recorded_traffic(),
+                     "kernel": "attn::fwd_kernel<BF16,128,...> (one launch per step)"},
+    }
+    if args.extras:
+        print("[bench] extras", file=sys.stderr, flush=True)
+        rec["extras"] = run_extras(device, max(args.steps // 5, 5), 3)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

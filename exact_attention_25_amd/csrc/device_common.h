@@ -49,6 +49,11 @@ struct BF16 {
     f32x2 v = {x, y};
     return __builtin_convertvector(v, V2);
   }
+  // acc + p.x + p.y in fp32 (one v_dot2 against (1, 1))
+  static __device__ __forceinline__ float sum2(V2 p, float acc) {
+    const V2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
 };
 
 struct FP16 {
@@ -62,6 +67,10 @@ struct FP16 {
   static __device__ __forceinline__ V2 cvt2(float x, float y) {
     f32x2 v = {x, y};
     return __builtin_convertvector(v, V2);
+  }
+  static __device__ __forceinline__ float sum2(V2 p, float acc) {
+    const V2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(p, one, acc, false);
   }
 };
 
