@@ -42,7 +42,6 @@ attn_status attn_validate(const attn_params* p, int for_backward) {
   if (for_backward) {
     if (p->mask) return ATTN_EUNSUPPORTED;
     if (p->dtype == ATTN_FP32) return ATTN_EUNSUPPORTED;
-    if (p->d != 128 && p->d != 64) return ATTN_EUNSUPPORTED;
   }
   return ATTN_OK;
 }
@@ -87,10 +86,36 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout: D [B,Hq,Nq] | nl2 [B,Hq,Nq] | (kv_chunks > 1) partial
+// dK and dV, [kv_chunks, B, Hkv, Nk, d] fp32 each.
+struct BwdWorkspace {
+  size_t rows, part, total;
+  int chunks;
+};
+
+BwdWorkspace bwd_workspace(const attn_params* p) {
+  BwdWorkspace w;
+  w.chunks = attn::bwd_kv_chunks(p->B, p->Hkv, p->Nk, p->Hq / p->Hkv);
+  w.rows = align256((size_t)p->B * p->Hq * p->Nq * sizeof(float));
+  w.part = w.chunks > 1 ? align256((size_t)w.chunks * p->B * p->Hkv * p->Nk * p->d * sizeof(float)) : 0;
+  w.total = 2 * w.rows + 2 * w.part;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t attn_bwd_workspace_bytes(const attn_params* p) {
   if (attn_validate(p, 1) != ATTN_OK) return 0;
-  const size_t delta = (size_t)p->B * p->Hq * p->Nq * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  const size_t t = bwd_workspace(p).total;
+  return t > 0 ? t : 256;
 }
 
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
@@ -111,7 +136,13 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   attn::BwdArgs a = {};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.delta = static_cast<float*>(workspace);
+  const BwdWorkspace ws = bwd_workspace(p);
+  char* wsp = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(wsp);
+  a.nl2 = reinterpret_cast<float*>(wsp + ws.rows);
+  a.part_dk = ws.part ? reinterpret_cast<float*>(wsp + 2 * ws.rows) : nullptr;
+  a.part_dv = ws.part ? reinterpret_cast<float*>(wsp + 2 * ws.rows + ws.part) : nullptr;
+  a.kv_chunks = ws.chunks;
   a.kv_lens = p->kv_lens;
   const Strides sq = strides_for(p->layout, p->Hq, p->Nq, p->d);
   const Strides sk = strides_for(p->layout, p->Hkv, p->Nk, p->d);

@@ -1,7 +1,54 @@
-// Backward attention kernels for gfx950 (being written).
-#include "attn_kernels.h"
-#include "device_common.h"
+// Backward attention: kernel instances, work split and dispatch (the kernels
+// are in attn_bwd_kernel.h).
+#include "attn_bwd_kernel.h"
 
 namespace attn {
-hipError_t launch_bwd16(const BwdArgs&, bool, bool, hipStream_t) { return hipErrorNotSupported; }
+
+// q-head chunks per kv-head for the dK/dV pass: the smallest divisor of the
+// group size that gives enough work-groups to fill the chip (every chunk
+// adds one partial dK/dV tensor to the workspace and to the final sum).
+int bwd_kv_chunks(int B, int Hkv, int Nk, int group) {
+  const long nkb = (Nk + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock;
+  const long base = (long)B * Hkv * nkb;
+  for (int c = 1; c < group; ++c)
+    if (group % c == 0 && base * c >= 2048) return c;
+  return group;
+}
+
+template <class E, int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
+  constexpr int NW_KV = kBwdKeysPerBlock / 32, BR = 64;
+  constexpr int NW_Q = 4, BC = 64;
+  // dQ, and D / nl2 per row for the dK/dV pass
+  if (a.Nq > 0) {
+    const int nqb = (a.Nq + NW_Q * 32 - 1) / (NW_Q * 32);
+    dim3 grid((unsigned)(a.B * a.Hq * nqb)), block(NW_Q * 64);
+    if (causal) hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, false>), grid, block, 0, st, a);
+  }
+  // dK / dV (after dQ: it reads D and nl2)
+  if (a.Nk > 0) {
+    const int nkb = (a.Nk + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock;
+    dim3 grid((unsigned)(a.B * a.Hkv * a.kv_chunks * nkb)), block(NW_KV * 64);
+    if (causal) hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, false>), grid, block, 0, st, a);
+    if (a.kv_chunks > 1) {
+      const int64_t n = (int64_t)a.B * a.Hkv * a.Nk * a.d;
+      const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+      hipLaunchKernelGGL((bwd_kv_reduce_kernel<typename E::T>), dim3(blocks), dim3(256), 0, st, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_bwd_e(const BwdArgs& a, bool causal, hipStream_t st) {
+  if (a.d > 64) return launch_bwd_t<E, 128>(a, causal, st);
+  return launch_bwd_t<E, 64>(a, causal, st);
+}
+
+hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, bool causal, hipStream_t st) {
+  return is_bf16 ? launch_bwd_e<BF16>(a, causal, st) : launch_bwd_e<FP16>(a, causal, st);
+}
+
 }  // namespace attn

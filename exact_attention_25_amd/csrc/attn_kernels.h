@@ -40,6 +40,9 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;          // [B, Hq, Nq] workspace: rowsum(dout * o)
+  float* nl2;            // [B, Hq, Nq] workspace: -lse * log2(e)
+  float* part_dk;        // [kv_chunks, B, Hkv, Nk, d] workspace (kv_chunks > 1)
+  float* part_dv;
   const int32_t* kv_lens;
   int64_t q_sb, q_sh, q_sn;   // q, o, dout, dq share these
   int64_t k_sb, k_sh, k_sn;   // k, v, dk, dv share these
@@ -48,7 +51,12 @@ struct BwdArgs {
   float scale;           // softmax scale
   float c;               // scale * log2(e)
   int32_t grad_f32;      // 1: dq/dk/dv are fp32, 0: input dtype
+  int32_t kv_chunks;     // q-head chunks per kv-head in the dK/dV pass
 };
+
+// Work split of the backward, shared by the workspace sizing and the launch.
+constexpr int kBwdKeysPerBlock = 128;   // keys per dK/dV work-group
+int bwd_kv_chunks(int B, int Hkv, int Nk, int group);
 
 hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, bool causal, bool mask, hipStream_t st);
 hipError_t launch_fwd32(const FwdArgs& a, bool causal, bool mask, hipStream_t st);

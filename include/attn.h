@@ -90,8 +90,8 @@ typedef struct {
  * backward's extra constraints.  Returns ATTN_OK, ATTN_EINVAL (null p, shapes
  * out of range (B, Nq, Nk < 0; Hq, Hkv, d < 1), Hq % Hkv != 0, causal with
  * Nq != Nk, bad enum, negative mask stride) or ATTN_EUNSUPPORTED (d outside
- * [8, 128] or d % 8 != 0; for the backward also an additive mask, an fp32
- * dtype, or d other than 64 or 128).  B == 0, Nq == 0 and Nk == 0 are
+ * [8, 128] or d % 8 != 0; for the backward also an additive mask or an fp32
+ * dtype).  B == 0, Nq == 0 and Nk == 0 are
  * valid: the first two make a call a no-op, the last makes every row fully
  * masked. */
 attn_status attn_validate(const attn_params* p, int for_backward);
@@ -109,7 +109,9 @@ attn_status attn_validate(const attn_params* p, int for_backward);
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
-/* Bytes of device workspace attn_bwd needs for *p (0 if p is invalid). */
+/* Bytes of device workspace attn_bwd needs for *p (0 if p is invalid): two
+ * [B, Hq, Nq] float arrays (D and -LSE*log2(e)) plus, when the q-heads of a
+ * kv-head are split over several work-groups, fp32 partial dK and dV sums. */
 size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /* Backward pass: gradients of <dout, O> with O = attention(q, k, v), with the

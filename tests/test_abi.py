@@ -73,7 +73,7 @@ def test_validate_backward_limits():
     assert bd.attn_validate(p, True) == bd.ATTN_EUNSUPPORTED
     p = _p(mask_ptr=16, mask_strides=(0, -1, 64))
     assert bd.attn_validate(p, False) == bd.ATTN_EINVAL
-    assert bd.attn_validate(None if False else _p(d=48), True) == bd.ATTN_EUNSUPPORTED
+    assert bd.attn_validate(_p(d=48), True) == bd.ATTN_OK
 
 
 def test_fwd_errors_return_before_launch():
@@ -95,7 +95,8 @@ def test_bwd_workspace_and_errors():
     p = _p(d=128)
     need = bd.attn_bwd_workspace_bytes(p)
     assert need >= 2 * 8 * 64 * 4 and need % 256 == 0
-    assert bd.attn_bwd_workspace_bytes(_p(d=48)) == 0
+    assert bd.attn_bwd_workspace_bytes(_p(d=44)) == 0
+    assert bd.attn_bwd_workspace_bytes(_p(dtype=bd.ATTN_FP32)) == 0
     args = [16] * 9
     assert lib.attn_bwd(ctypes.byref(p), *args, bd.ATTN_FP32, 16, need - 1, None) == bd.ATTN_EWORKSPACE
     assert lib.attn_bwd(ctypes.byref(p), *args, bd.ATTN_FP32, None, need, None) == bd.ATTN_EWORKSPACE

@@ -1,0 +1,126 @@
+"""GPU backward parity: attn_bwd (recompute from LSE) against the fp64 oracle.
+
+The backward consumes the forward's own (O, LSE) from the GPU path, as a
+caller would.  Gradients are fp32 (the default); the bar is max-abs 2e-2 on
+dQ, dK and dV, plus a relative-RMS bound.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from exact_attention_25_amd import inputs
+from oracle import ref_bwd, ref_bwd_group
+from tests.gpu_util import from_layout, host, make_case, to_device, to_layout
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TOL_REL_RMS = 1e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(w, x, *, layout="bhnd", causal=False, scale=None, grad_dtype="fp32"):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    t = {n: to_device(to_layout(x[n + "_raw"], layout), w.dtype) for n in ("q", "k", "v", "do")}
+    lens = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).cuda()
+    o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], layout=layout, causal=causal, scale=scale,
+                         kv_lens=lens)
+    dq, dk, dv = bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], layout=layout,
+                             causal=causal, scale=scale, kv_lens=lens, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check(name, got, ref, tol=TOL, rel=TOL_REL_RMS):
+    g = host(got)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite"
+    err = np.abs(g - ref)
+    mx = float(err.max()) if err.size else 0.0
+    assert mx <= tol, f"{name}: max-abs {mx:.3e} > {tol}"
+    rr = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    if rr > 0:
+        rel_rms = float(np.sqrt(np.mean(err ** 2))) / rr
+        assert rel_rms <= rel, f"{name}: rel-rms {rel_rms:.3e}"
+    return mx
+
+
+SMALL = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, layout, scale
+    ("bf16_causal_gqa_lens", 2, 8, 2, 200, 200, 128, "bf16", True, (90, 200), "bhnd", None),
+    ("fp16_noncausal_ragged", 2, 2, 2, 150, 90, 64, "fp16", False, None, "bhnd", None),
+    ("bf16_bnhd_gqa", 1, 4, 1, 130, 130, 128, "bf16", False, None, "bnhd", 0.2),
+    ("fp16_d40_cross_lens", 2, 2, 2, 257, 77, 40, "fp16", False, (20, 77), "bhnd", None),
+    ("bf16_lens_zero", 3, 2, 2, 70, 90, 64, "bf16", False, (0, 2), "bhnd", None),
+    ("bf16_d96_causal", 1, 2, 2, 300, 300, 96, "bf16", True, None, "bhnd", None),
+    ("fp16_many_heads_chunks", 1, 16, 1, 96, 96, 128, "fp16", True, None, "bhnd", None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_small(gpu_lib, case):
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, layout, scale = case
+    _say(f"[bwd-small] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens, with_do=True)
+    dq, dk, dv = _run(w, x, layout=layout, causal=causal, scale=scale)
+    dQ, dK, dV, _, _ = ref_bwd(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=scale,
+                               kv_lens=x["kv_lens"])
+    _check(name + " dq", from_layout(host(dq), layout), dQ)
+    _check(name + " dk", from_layout(host(dk), layout), dK)
+    _check(name + " dv", from_layout(host(dv), layout), dV)
+
+
+def test_backward_16bit_gradients(gpu_lib):
+    _say("[bwd] 16-bit gradient outputs")
+    w, x = make_case(1, 4, 2, 160, 160, 64, "bf16", seed=11, with_do=True)
+    dq, dk, dv = _run(w, x, causal=True, grad_dtype="bf16")
+    import torch
+    assert dq.dtype == torch.bfloat16
+    dQ, dK, dV, _, _ = ref_bwd(x["q"], x["k"], x["v"], x["do"], causal=True)
+    # bf16 outputs: the output rounding alone is up to half an ulp of |x|
+    for nm, g, r in (("dq", dq, dQ), ("dk", dk, dK), ("dv", dv, dV)):
+        _check(nm, g, r, tol=2e-2 + 2 ** -8 * float(np.abs(r).max()), rel=2e-2)
+
+
+def test_backward_is_deterministic(gpu_lib):
+    import torch
+    _say("[bwd] determinism")
+    w, x = make_case(1, 16, 1, 200, 200, 128, "bf16", seed=12, with_do=True)
+    a = _run(w, x, causal=True)
+    b = _run(w, x, causal=True)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_workload_causal_gqa_backward(gpu_lib):
+    """Full-size causal GQA backward: one (batch, kv-head) group exactly
+    (all 16 q-heads, all keys), plus identities over every group."""
+    import torch
+    w = inputs.WORKLOADS["causal_gqa_bf16_b4_h32_kv2_n8192_d128"]
+    _say("[bwd-workload] generating inputs")
+    x = inputs.make_inputs(w)
+    _say("[bwd-workload] GPU forward + backward")
+    dq, dk, dv = _run(w, x, causal=True)
+    G = w.Hq // w.Hkv
+    # identities at full size: sum_j dK_j = 0, sum_j dV_j = sum_rows dO
+    dks = dk.double().sum(dim=2)
+    assert float(dks.abs().max()) < 5e-2, float(dks.abs().max())
+    do = to_device(x["do_raw"], w.dtype).double()
+    dvs = dv.double().sum(dim=2)
+    ref_dvs = do.reshape(w.B, w.Hkv, G, w.Nq, w.d).sum(dim=(2, 3))
+    assert float((dvs - ref_dvs).abs().max()) < 1.0, float((dvs - ref_dvs).abs().max())
+    b, g = w.B - 1, w.Hkv - 1
+    _say(f"[bwd-workload] oracle for batch {b}, kv-head {g} ({G} q-heads)")
+    dQ, dK, dV, _, _ = ref_bwd_group(x["q"], x["k"], x["v"], x["do"], b, g, causal=True,
+                                     kv_lens=x["kv_lens"])
+    _check("dq", dq[b, g * G:(g + 1) * G], dQ)
+    _check("dk", dk[b, g], dK)
+    _check("dv", dv[b, g], dV)
