@@ -8,7 +8,12 @@ TFLOP/s (4*B*H*N^2*d per call), the roofline position of the forward kernel
 oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--extras] [--no-cpu-baseline] [--copy-calibration]
+                    [--pass fwd|bwd] [--extras] [--no-cpu-baseline]
+                    [--copy-calibration]
+
+--pass bwd times attn_bwd instead (from the forward's O and LSE), e.g. on
+--workload causal_gqa_bf16_b4_h32_kv2_n8192_d128; its CPU baseline is the
+oracle's backward on one (batch, kv-head) group.
 
 --extras also times the other workloads (the ViT, UNet self/cross, causal
 GQA forward and backward, and the long-context sweep) and adds them to the
@@ -30,9 +35,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS & % of bf16 MFMA peak at B8 H32 N4096 d128"
 DEFAULT_WORKLOAD = "long_bf16_b8_h32_n4096_d128"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_bf16_b8_h32_n4096_d128_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_bf16_b8_h32_n4096_d128_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_25_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "device_common.h", "attn_kernels.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_kernel.h", "device_common.h",
+                            "attn_kernels.h")]
 
 
 def kernel_source_hash() -> str:
@@ -92,30 +98,48 @@ def workload_inputs(w, device, with_do=False):
     return x, t
 
 
-def cpu_baseline(w, x, budget_s=15.0):
-    """The fp64 oracle on the first heads of batch 0, until ~budget_s of CPU
+def cpu_baseline(w, x, budget_s=15.0, backward=False):
+    """The fp64 oracle on (batch, head) pairs in order, until ~budget_s of CPU
     time; returns a dict in the metric's unit (TFLOP/s)."""
     from threadpoolctl import threadpool_info
     from exact_attention_25_amd import accounting as acc
-    from oracle import ref_fwd
+    from oracle import ref_bwd_group, ref_fwd
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    heads = 0
+    G = w.Hq // w.Hkv
+    done = 0
     t0 = time.perf_counter()
-    while heads < w.Hq:
-        sl = slice(heads, heads + 1)
-        g = heads // (w.Hq // w.Hkv)
-        lens = None if x["kv_lens"] is None else x["kv_lens"][:1]
-        ref_fwd(x["q"][:1, sl], x["k"][:1, g:g + 1], x["v"][:1, g:g + 1], causal=w.causal,
-                kv_lens=lens)
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    if backward:
+        # one (batch, kv-head) group per oracle call: G heads
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                ref_bwd_group(x["q"], x["k"], x["v"], x["do"], b, g, causal=w.causal,
+                              kv_lens=x["kv_lens"])
+                done += G
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        flops = acc.bwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
+        what = "fp64 numpy oracle backward (incl. its forward)"
+    else:
+        for b in range(w.B):
+            for h in range(w.Hq):
+                g = h // G
+                lens = None if x["kv_lens"] is None else x["kv_lens"][b:b + 1]
+                ref_fwd(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, g:g + 1],
+                        x["v"][b:b + 1, g:g + 1], causal=w.causal, kv_lens=lens)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        flops = acc.fwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
+        what = "fp64 numpy oracle forward"
     dt = time.perf_counter() - t0
-    flops = acc.fwd_flops(1, heads, w.Nq, w.Nk, w.d, w.causal)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle forward on {heads} of {w.B * w.Hq} heads "
-                      f"(batch 0, heads 0..{heads - 1}) of {w.name}, {dt:.1f} s"}
+            "sample": f"{what} on the first {done} of {w.B * w.Hq} (batch, head) pairs of "
+                      f"{w.name}, {dt:.1f} s; TFLOP/s counted like the GPU value"}
 
 
 def run_extras(device, steps, warmup):
@@ -165,6 +189,8 @@ def main():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward from the forward's O/LSE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the attention of every (batch, head) is "
@@ -191,7 +217,8 @@ def main():
             raise SystemExit(f"unknown workload {args.workload}")
         w = inputs.sweep_workload(int(m.group(1)))
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
-    x, t = workload_inputs(w, device)
+    bwd = args.which == "bwd"
+    x, t = workload_inputs(w, device, with_do=bwd)
 
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
@@ -203,15 +230,25 @@ def main():
         print("[bench] copy calibration: 3 x 1 GiB device copies", file=sys.stderr, flush=True)
         del src, dst
 
-    fn = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"])
+    fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"])
+    if bwd:
+        o, lse = fwd()
+        ws = torch.empty(bd.attn_bwd_workspace_bytes(bd.make_params(
+            w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, bd.ATTN_BF16 if w.dtype == "bf16" else bd.ATTN_FP16,
+            causal=w.causal)), dtype=torch.uint8, device=device)
+        fn = lambda: bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal,
+                                 kv_lens=t["kv_lens"], workspace=ws)
+        flops = acc.bwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    else:
+        fn = fwd
+        flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     ms, wall = time_calls(fn, args.steps, args.warmup, stream)
 
-    flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
     tflops = flops / ms / 1e9
     peak = acc.PEAK_TFLOPS[w.dtype]
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not bwd else "attention bwd TFLOPS (10*B*H*N^2*d, halved for causal)",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -222,22 +259,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) q/k/v, numpy PCG64, rounded to bf16)",
+        "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype})",
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "Hkv": w.Hkv, "N": w.Nq,
-                   "d": w.d, "causal": w.causal, "mask": None, "pass": "forward"},
+                   "d": w.d, "causal": w.causal, "mask": None, "key_padding": w.lens is not None,
+                   "pass": "backward" if bwd else "forward"},
         "pct_of_peak": round(tflops / peak * 100, 2),
         "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": recorded_traffic(),
-                     "kernel": "attn::fwd_kernel<BF16,128,...> (one launch per step)"},
+                     "traffic": None if bwd else recorded_traffic(),
+                     "kernel": ("attn::bwd_q_kernel + attn::bwd_kv_kernel (+ reduce), one call per step"
+                                if bwd else "attn::fwd_kernel<BF16,128,8,64> (one launch per step)")},
     }
     if args.extras:
         print("[bench] extras", file=sys.stderr, flush=True)
         rec["extras"] = run_extras(device, max(args.steps // 5, 5), 3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, x)
+        rec["cpu_baseline"] = cpu_baseline(w, x, backward=bwd)
     print(json.dumps(rec), flush=True)
 
 
