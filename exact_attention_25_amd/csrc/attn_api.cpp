@@ -92,17 +92,18 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout: D [B,Hq,Nq] | nl2 [B,Hq,Nq] | (kv_chunks > 1) partial
-// dK and dV, [kv_chunks, B, Hkv, Nk, d] fp32 each.
+// Workspace layout: D [B,Hq,ld] | nl2 [B,Hq,ld] | (kv_chunks > 1) partial
+// dK and dV, [kv_chunks, B, Hkv, Nk, d] fp32 each; ld = Nq rounded up to 64.
 struct BwdWorkspace {
   size_t rows, part, total;
-  int chunks;
+  int chunks, ld;
 };
 
 BwdWorkspace bwd_workspace(const attn_params* p) {
   BwdWorkspace w;
   w.chunks = attn::bwd_kv_chunks(p->B, p->Hkv, p->Nk, p->Hq / p->Hkv);
-  w.rows = align256((size_t)p->B * p->Hq * p->Nq * sizeof(float));
+  w.ld = (p->Nq + 63) / 64 * 64;
+  w.rows = align256((size_t)p->B * p->Hq * w.ld * sizeof(float));
   w.part = w.chunks > 1 ? align256((size_t)w.chunks * p->B * p->Hkv * p->Nk * p->d * sizeof(float)) : 0;
   w.total = 2 * w.rows + 2 * w.part;
   return w;
@@ -143,6 +144,7 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.part_dk = ws.part ? reinterpret_cast<float*>(wsp + 2 * ws.rows) : nullptr;
   a.part_dv = ws.part ? reinterpret_cast<float*>(wsp + 2 * ws.rows + ws.part) : nullptr;
   a.kv_chunks = ws.chunks;
+  a.ld_rows = ws.ld;
   a.kv_lens = p->kv_lens;
   const Strides sq = strides_for(p->layout, p->Hq, p->Nq, p->d);
   const Strides sk = strides_for(p->layout, p->Hkv, p->Nk, p->d);

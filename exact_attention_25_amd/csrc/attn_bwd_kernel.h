@@ -218,8 +218,9 @@ struct BwdQ {
     const float dtot = add_with_other_half(dsum);
     if (qrow >= a.Nq) return;
     if (hl == 0) {
-      a.delta[rid] = dtot;
-      a.nl2[rid] = nl2;
+      const int64_t wid_row = ((int64_t)b * a.Hq + h) * a.ld_rows + qrow;
+      a.delta[wid_row] = dtot;
+      a.nl2[wid_row] = nl2;
     }
     const int64_t base = b * a.q_sb + h * a.q_sh + qrow * a.q_sn;
 #pragma unroll
@@ -282,9 +283,16 @@ struct BwdKV {
   using H4 = f16x4;
 
   // Q and dO tile rows q0..q0+BR-1 of head h, rows clamped onto valid memory
-  // (rows >= Nq get P = 0 below).
+  // (rows >= Nq get P = 0 below), and the tile's nl2 and D rows (16 bytes =
+  // 4 rows per lane: lanes 0..BR/4-1 nl2, the next BR/4 lanes D) into sb.
   static __device__ __forceinline__ void issue(const BwdArgs& a, int b, int h, int q0, char* qb,
-                                               char* db, int wave, int lane) {
+                                               char* db, char* sb, int wave, int lane) {
+    if (wave == 0 && lane < BR / 2) {
+      // rows q0 .. q0+BR-1 lie inside the head's ld_rows-long block
+      const float* src = (lane < BR / 4 ? a.nl2 : a.delta) + ((int64_t)b * a.Hq + h) * a.ld_rows +
+                         q0 + (lane % (BR / 4)) * 4;
+      dma16(src, sb);
+    }
     const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh;
     const T* dp = (const T*)a.dout + b * a.q_sb + h * a.q_sh;
     const int dch = a.d / 8;
@@ -316,7 +324,7 @@ struct BwdKV {
     return concat4<H8, H4>(lo, hi);
   }
 
-  static __device__ void run(const BwdArgs& a, char* q0b, char* d0b, char* q1b, char* d1b) {
+  static __device__ void run(const BwdArgs& a, char* q0b, char* q1b) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, l32 = lane & 31;
@@ -362,25 +370,33 @@ struct BwdKV {
     const int n_qt = (key0 < kv_limit && q_start < a.Nq) ? (a.Nq - q_start + BR - 1) / BR : 0;
     const int HS = a.group / a.kv_chunks;
     const int h0 = g * a.group + chunk * HS;
-    const int n_t = n_qt * HS;   // (head, q-tile) pairs
+    const int n_t = n_qt * HS;   // (head, q-tile) pairs, head-major
 
-    if (n_t > 0) issue(a, b, h0, q_start, q0b, d0b, wave, lane);
+    // stage buffers: [Q tile | dO tile | nl2, D] each
+    char* const sbuf[2] = {q0b + 2 * TILE_BYTES, q1b + 2 * TILE_BYTES};
+    if (n_t > 0) issue(a, b, h0, q_start, q0b, q0b + TILE_BYTES, sbuf[0], wave, lane);
+    int q0 = q_start;              // tile t (its head needs no tracking here)
+    int hn = h0, qn = q_start;     // tile t + 1
     for (int t = 0; t < n_t; ++t) {
       char* qc = (t & 1) ? q1b : q0b;
-      char* dc = (t & 1) ? d1b : d0b;
+      char* dc = qc + TILE_BYTES;
+      const char* sc = sbuf[t & 1];
       __builtin_amdgcn_s_waitcnt(0);
       convert_own_slots<E, SPW, NW>(qc, wave, lane);
       convert_own_slots<E, SPW, NW>(dc, wave, lane);
       __syncthreads();
-      if (t + 1 < n_t) {
-        const int hn = h0 + (t + 1) / n_qt, qn = q_start + ((t + 1) % n_qt) * BR;
-        issue(a, b, hn, qn, (t & 1) ? q0b : q1b, (t & 1) ? d0b : d1b, wave, lane);
+      qn += BR;
+      if (qn >= a.Nq) {
+        qn = q_start;
+        ++hn;
       }
-      const int h = h0 + t / n_qt;
-      const int q0 = q_start + (t % n_qt) * BR;
-      if (CAUSAL && q0 + BR - 1 < kw0) continue;  // no row of the tile sees this wave's keys
-      const float* nl2p = a.nl2 + ((int64_t)b * a.Hq + h) * a.Nq;
-      const float* dlp = a.delta + ((int64_t)b * a.Hq + h) * a.Nq;
+      if (t + 1 < n_t) {
+        char* qx = (t & 1) ? q0b : q1b;
+        issue(a, b, hn, qn, qx, qx + TILE_BYTES, sbuf[(t + 1) & 1], wave, lane);
+      }
+      const int qt0 = q0;
+      q0 = qn;
+      if (CAUSAL && qt0 + BR - 1 < kw0) continue;  // no row of the tile sees this wave's keys
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -389,20 +405,22 @@ struct BwdKV {
           s = FP16::mfma(rowfrag(qc, qb * 32 + l32, ks, hl), kf[ks], s);
           dp = FP16::mfma(rowfrag(dc, qb * 32 + l32, ks, hl), vf[ks], dp);
         }
-        // rows of register r: q0 + qb*32 + (r/4)*8 + 4 hl + r%4
+        // rows of register r: qt0 + qb*32 + (r/4)*8 + 4 hl + r%4
         H8 pp[2], dsp[2];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int qr0 = q0 + qb * 32 + gq * 8 + hl * 4;
+          const int lr = qb * 32 + gq * 8 + hl * 4;   // local row of e = 0
+          const f32x4 nl = *(const LDS_AS f32x4*)(const LDS_AS void*)(sc + lr * 4);
+          const f32x4 dd = *(const LDS_AS f32x4*)(const LDS_AS void*)(sc + BR * 4 + lr * 4);
           float pv[4], dsv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = gq * 4 + e;
-            const int qr = min(qr0 + e, a.Nq - 1);
-            const bool vis = key < kv_limit && qr0 + e < a.Nq && (!CAUSAL || key <= qr0 + e);
-            const float p = vis ? fast_exp2(__builtin_fmaf(s[r], a.c, nl2p[qr])) : 0.f;
-            pv[e] = p;
-            dsv[e] = p * (dp[r] - dlp[qr]);
+            const int qr = qt0 + lr + e;
+            const bool vis = key < kv_limit && qr < a.Nq && (!CAUSAL || key <= qr);
+            const float p = fast_exp2(__builtin_fmaf(s[r], a.c, nl[e]));
+            pv[e] = vis ? p : 0.f;
+            dsv[e] = vis ? p * (dp[r] - dd[e]) : 0.f;
           }
           const int t2 = gq >> 1, half = (gq & 1) * 4;
           const f16x2 p01 = FP16::cvt2(pv[0], pv[1]), p23 = FP16::cvt2(pv[2], pv[3]);
@@ -458,11 +476,10 @@ struct BwdKV {
 template <class E, int D, int NW, int BR, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
   using K = BwdKV<E, D, NW, BR, CAUSAL>;
-  __shared__ __attribute__((aligned(1024))) char q0[K::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char d0[K::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char q1[K::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char d1[K::TILE_BYTES];
-  K::run(a, q0, d0, q1, d1);
+  // per stage: Q tile | dO tile | nl2 and D of the tile's rows
+  __shared__ __attribute__((aligned(1024))) char s0[2 * K::TILE_BYTES + 2 * BR * 4];
+  __shared__ __attribute__((aligned(1024))) char s1[2 * K::TILE_BYTES + 2 * BR * 4];
+  K::run(a, s0, s1);
 }
 
 // Sum of the per-chunk partial dK / dV in a fixed order (deterministic).

@@ -39,8 +39,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;          // [B, Hq, Nq] workspace: rowsum(dout * o)
-  float* nl2;            // [B, Hq, Nq] workspace: -lse * log2(e)
+  float* delta;          // [B, Hq, ld_rows] workspace: D = rowsum(P * dP)
+  float* nl2;            // [B, Hq, ld_rows] workspace: -lse * log2(e)
   float* part_dk;        // [kv_chunks, B, Hkv, Nk, d] workspace (kv_chunks > 1)
   float* part_dv;
   const int32_t* kv_lens;
@@ -52,6 +52,7 @@ struct BwdArgs {
   float c;               // scale * log2(e)
   int32_t grad_f32;      // 1: dq/dk/dv are fp32, 0: input dtype
   int32_t kv_chunks;     // q-head chunks per kv-head in the dK/dV pass
+  int32_t ld_rows;       // row stride of delta / nl2 per (b, h): Nq rounded up to 64
 };
 
 // Work split of the backward, shared by the workspace sizing and the launch.
