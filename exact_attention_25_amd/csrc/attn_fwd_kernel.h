@@ -8,9 +8,9 @@
 //
 // Work decomposition: one work-group of NW waves per (batch, q-head, block of
 // NW*32 query rows); each wave owns 32 rows, whose Q fragments stay in
-// registers.  K/V tiles of BC keys stream through LDS, double-buffered and
-// filled by direct global->LDS loads: the load of tile j+1 runs while tile j
-// is in use.  With NW = 8 (two waves per SIMD) the waves of a SIMD overlap
+// registers.  K/V tiles of BC keys stream through LDS (padded row pitches),
+// double-buffered and filled by direct global->LDS loads: the load of tile
+// j+1 runs while tile j is in use.  With NW = 8 (two waves per SIMD) the waves of a SIMD overlap
 // each other's LDS and VALU latency.
 //
 // Per KV tile and wave:
@@ -41,14 +41,25 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: p stays <= 256
 template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
 struct FwdKernel {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BC * D * 2;     // one K or V tile
+  // LDS row pitches in 16-byte slots.  K rows get one pad slot: the 16 rows
+  // that one read instruction touches at a time (same chunk) then fall on 16
+  // different bank groups.  V rows get a pitch of 64 (mod 256) bytes: the
+  // transposed read takes 4 consecutive rows x 64 bytes per half-wave, which
+  // then cover all 64 banks.  Every read address is a per-lane base plus a
+  // compile-time offset.
+  static constexpr int KPS = CPR + 1;
+  static constexpr int VPS = CPR + 4;
+  static constexpr int KP = KPS * 16, VP = VPS * 16;   // pitches in bytes
+  static constexpr int K_BYTES = BC * KP, V_BYTES = BC * VP;
+  static constexpr int K_INS = (BC * KPS + 63) / 64;   // DMA instructions per K tile
+  static constexpr int V_INS = (BC * VPS + 63) / 64;
+  static constexpr int K_IPW = (K_INS + NW - 1) / NW;  // ... per wave
+  static constexpr int V_IPW = (V_INS + NW - 1) / NW;
   static constexpr int ROWS = NW * 32;              // query rows per block
-  static constexpr int SPW = BC * CPR / (NW * 64);  // DMA slots per wave per tensor
   static constexpr int KB = BC / 32;                // 32-key blocks per tile
   static constexpr int KS = D / 16;                 // k-steps of QK^T
   static constexpr int DT = D / 32;                 // 32-wide d tiles of O
   static constexpr int PT = BC / 16;                // k-steps of PV
-  static_assert(BC * CPR % (NW * 64) == 0, "tile must split evenly into DMA slots");
 
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -59,54 +70,48 @@ struct FwdKernel {
     int b, h;                   // batch and q-head of this block
     int q_w0;                   // first query row of this wave
     int kv_limit;               // keys >= kv_limit are excluded
-    int nk;                     // keys in memory
     int n_act;                  // tiles this wave has to visit (causal)
-    int dchunks;                // 16-byte chunks per row in memory (d / 8)
-    const T* kp;
-    const T* vp;
-    int64_t k_sn, v_sn;
-    int koff[SPW], voff[SPW];   // element offset of this lane's DMA chunks in a tile
+    const char* kp;             // K / V of this (batch, kv-head), key 0
+    const char* vp;
+    int64_t k_tile, v_tile;     // bytes between consecutive tiles
+    int64_t k_end, v_end;       // bytes from kp / vp to the end of key nk-1
+    // per DMA instruction of this lane: byte offset (within a tile) of the
+    // chunk it copies, kBufOutOfRange for pad slots and columns past d
+    uint32_t koff[K_IPW], voff[V_IPW];
+    int kbase, vbase;           // per-lane LDS byte offsets of the read patterns
     float c;                    // scale * log2(e)
     V8 qf[KS];                  // Q fragments (B operand of S^T = K Q^T)
     f32x16 acc[DT];             // O^T accumulators
     float m_run, l_run;
   };
 
-  // DMA slot s of a tile (16 bytes): its row and the element offsets of the
-  // K and V chunks that land there (swizzled, clamped to the head dim).
-  static __device__ __forceinline__ void slot_chunks(int s, int dchunks, int& row, int& kc,
-                                                     int& vc) {
-    row = s / CPR;
-    const int p = s % CPR;
-    kc = min(p ^ swz_k<CPR>(row), dchunks - 1) * 8;
-    vc = min(p ^ swz_v<CPR>(row), dchunks - 1) * 8;
+  // Byte offset, within a tile of row pitch sn elements, of the chunk that
+  // lane copies in DMA instruction `ins` of a tile with `ps` slots per row.
+  static __device__ __forceinline__ uint32_t dma_offset(int ins, int lane, int ps, int dchunks,
+                                                        int64_t sn) {
+    const int s = ins * 64 + lane;
+    const int r = s / ps, ch = s % ps;
+    if (r >= BC || ch >= dchunks) return kBufOutOfRange;
+    return (uint32_t)((r * sn + ch * 8) * 2);
   }
 
-  // Direct loads of one K tile and one V tile (keys j0..j0+BC-1).  In the
-  // last, partial tile the rows beyond the last key are clamped onto valid
-  // memory; chunks beyond the head dimension are clamped likewise.  Those
-  // extra keys are masked to -inf and the extra K columns meet zero Q
-  // columns, so their (finite) values never reach the result.
+  // Direct loads of one K tile and one V tile (keys j0..j0+BC-1), through
+  // buffer resources that end at key nk-1: rows past it, pad slots and
+  // columns past d read as zero.  Keys past the end are masked to -inf and
+  // zero K columns meet zero Q columns, so none of them reach the result.
   static __device__ __forceinline__ void issue(const State& st, int j0, char* kb, char* vb) {
-    if (j0 + BC <= st.nk) {
-      const T* kbase = st.kp + (int64_t)j0 * st.k_sn;
-      const T* vbase = st.vp + (int64_t)j0 * st.v_sn;
+    const int64_t ko = (int64_t)(j0 / BC) * st.k_tile, vo = (int64_t)(j0 / BC) * st.v_tile;
+    const BufRsrc rk = make_rsrc(st.kp + ko, (uint32_t)min(st.k_end - ko, (int64_t)kBufLimit));
+    const BufRsrc rv = make_rsrc(st.vp + vo, (uint32_t)min(st.v_end - vo, (int64_t)kBufLimit));
 #pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const int slot0 = (i * NW + st.wave) * 64;
-        dma16(kbase + st.koff[i], kb + slot0 * 16);
-        dma16(vbase + st.voff[i], vb + slot0 * 16);
-      }
-    } else {
+    for (int i = 0; i < K_IPW; ++i) {
+      const int ins = i * NW + st.wave;
+      if (ins < K_INS) dma16_buf(rk, st.koff[i], kb + ins * 1024);
+    }
 #pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const int slot0 = (i * NW + st.wave) * 64;
-        int row, kc, vc;
-        slot_chunks(slot0 + st.lane, st.dchunks, row, kc, vc);
-        const int64_t grow = min(j0 + row, st.nk - 1);
-        dma16(st.kp + grow * st.k_sn + kc, kb + slot0 * 16);
-        dma16(st.vp + grow * st.v_sn + vc, vb + slot0 * 16);
-      }
+    for (int i = 0; i < V_IPW; ++i) {
+      const int ins = i * NW + st.wave;
+      if (ins < V_INS) dma16_buf(rv, st.voff[i], vb + ins * 1024);
     }
   }
 
@@ -121,9 +126,7 @@ struct FwdKernel {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
-        const int row = k * 32 + st.l32;
-        const int c = (ks * 2 + st.hl) ^ swz_k<CPR>(row);
-        const V8 kf = lds_read16<V8>(kbuf + row * (D * 2) + c * 16);
+        const V8 kf = lds_read16<V8>(kbuf + st.kbase + k * 32 * KP + ks * 32);
         s[k] = E::mfma(kf, st.qf[ks], s[k]);
       }
     }
@@ -189,17 +192,13 @@ struct FwdKernel {
     st.l_run += lsum;
 
     // O^T += V_j^T P^T
-    const int grp = st.lane >> 4, gi = st.lane & 15;
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int row = t * 16 + 4 * (grp >> 1) + (gi >> 2);
-        const int col = dt * 32 + 16 * (grp & 1) + 4 * (gi & 3);
-        const int chunk = col >> 3, within = (col & 7) * 2;
-        const V4 lo = lds_read_tr4<V4>(vbuf + row * (D * 2) + ((chunk ^ swz_v<CPR>(row)) << 4) + within);
-        const int row2 = row + 8;
-        const V4 hi = lds_read_tr4<V4>(vbuf + row2 * (D * 2) + ((chunk ^ swz_v<CPR>(row2)) << 4) + within);
+        const char* p = vbuf + st.vbase + t * 16 * VP + dt * 64;
+        const V4 lo = lds_read_tr4<V4>(p);
+        const V4 hi = lds_read_tr4<V4>(p + 8 * VP);
         st.acc[dt] = E::mfma(concat4<V8, V4>(lo, hi), pf[t], st.acc[dt]);
       }
     }
@@ -240,19 +239,28 @@ struct FwdKernel {
     const int n_tiles = (kv_end + BC - 1) / BC;
     // causal: a wave sees no key beyond its last row
     st.n_act = CAUSAL ? min(n_tiles, (st.q_w0 + 31) / BC + 1) : n_tiles;
-    st.dchunks = a.d / 8;
-    st.nk = a.Nk;
+    const int dchunks = a.d / 8;
     st.c = a.c;
-    st.k_sn = a.k_sn;
-    st.v_sn = a.v_sn;
-    st.kp = (const T*)a.k + b * a.k_sb + g * a.k_sh;
-    st.vp = (const T*)a.v + b * a.v_sb + g * a.v_sh;
+    st.kp = (const char*)((const T*)a.k + b * a.k_sb + g * a.k_sh);
+    st.vp = (const char*)((const T*)a.v + b * a.v_sb + g * a.v_sh);
+    st.k_tile = (int64_t)BC * a.k_sn * 2;
+    st.v_tile = (int64_t)BC * a.v_sn * 2;
+    st.k_end = ((int64_t)(a.Nk - 1) * a.k_sn + a.d) * 2;
+    st.v_end = ((int64_t)(a.Nk - 1) * a.v_sn + a.d) * 2;
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      int row, kc, vc;
-      slot_chunks((i * NW + st.wave) * 64 + st.lane, st.dchunks, row, kc, vc);
-      st.koff[i] = row * (int)st.k_sn + kc;
-      st.voff[i] = row * (int)st.v_sn + vc;
+    for (int i = 0; i < K_IPW; ++i)
+      st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn);
+#pragma unroll
+    for (int i = 0; i < V_IPW; ++i)
+      st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn);
+    // K read: lane holds key row l32 (+32 k), chunk 2 ks + hl.
+    st.kbase = st.l32 * KP + st.hl * 16;
+    // V transposed read: in each 16-lane group lane i points at row
+    // 4 (group / 2) + i / 4 (+16 t, +8), column 16 (group % 2) + 4 (i % 4)
+    // (+32 dt), so that lane l gets column l of four consecutive rows.
+    {
+      const int grp = st.lane >> 4, gi = st.lane & 15;
+      st.vbase = (4 * (grp >> 1) + (gi >> 2)) * VP + (16 * (grp & 1) + 4 * (gi & 3)) * 2;
     }
 
     const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh;
@@ -306,10 +314,10 @@ template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void fwd_kernel(FwdArgs a) {
   using K = FwdKernel<E, D, NW, BC, CAUSAL, MASK>;
-  __shared__ __attribute__((aligned(1024))) char k0[K::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v0[K::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k1[K::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v1[K::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[K::V_BYTES];
   K::run(a, k0, v0, k1, v1);
 }
 

@@ -1,0 +1,383 @@
+// Software-pipelined forward attention kernel for gfx950 (16-bit inputs,
+// no causal mask, no additive mask).
+//
+// Same arithmetic as FwdKernel in attn_fwd_kernel.h -- the tiled online
+// softmax of "FlashAttention技术解析：优化Transformer注意力计算效率"
+// (jsqmd.com/news/722897) §2.2 with the single final normalisation of its
+// §4.1 -- and bit-identical results; only the order of issue differs.
+//
+// Each wave owns 32 query rows; 8 waves (two per SIMD) share K/V tiles of BC
+// keys that stream through LDS, filled by direct buffer->LDS loads.  K runs
+// one tile ahead of V: iteration j computes S of tile j+1 while it finishes
+// tile j, so the matrix cores have independent work while the vector unit
+// evaluates the exponentials:
+//
+//   phase 1 (NQ steps):  one QK^T MFMA of tile j+1 per step, interleaved with
+//                        part of tile j's exponentials (p = exp2(s*c - m),
+//                        row sum, conversion to the 16-bit P operand);
+//   phase 2 (NP steps):  one PV MFMA of tile j per step; the first half of
+//                        the steps finish the exponentials (each 16-key
+//                        chunk before its first PV), the second half reduce
+//                        tile j+1's row maximum.
+//
+// A single wave hides only a handful of vector instructions under each MFMA,
+// so the vector work is spread evenly over both phases.  sched_barrier fences
+// keep the compiler from regrouping the steps, and empty asm statements pin
+// the running sum and maximum to their step (otherwise they are sunk to the
+// end of the block as one serial chain).  LDS fragments are read two steps
+// ahead of their MFMA.
+//
+// Tiles that reach past the key range (kv_lens, ragged Nk) are masked after
+// the main block and their maximum recomputed; the lazy rescale (reference
+// point moved only when a tile's maximum exceeds it by more than TH) follows.
+#pragma once
+
+#include "attn_kernels.h"
+#include "device_common.h"
+
+namespace attn {
+
+template <class E, int D, int BC>
+struct FwdPipeKernel {
+  static constexpr float TH = 8.0f;                 // rescale threshold, log2 units
+  static constexpr int NW = 8;                      // waves per work-group
+  static constexpr int ROWS = NW * 32;              // query rows per work-group
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  // LDS row pitches in 16-byte slots: one pad slot per K row (the 16 rows one
+  // K read touches at a time fall on distinct banks), four per V row (the
+  // transposed read takes 4 rows x 64 bytes per half-wave).
+  static constexpr int KPS = CPR + 1;
+  static constexpr int VPS = CPR + 4;
+  static constexpr int KP = KPS * 16, VP = VPS * 16;
+  static constexpr int K_BYTES = BC * KP, V_BYTES = BC * VP;
+  static constexpr int K_INS = (BC * KPS + 63) / 64;   // load instructions per K tile
+  static constexpr int V_INS = (BC * VPS + 63) / 64;
+  static constexpr int K_IPW = (K_INS + NW - 1) / NW;  // ... per wave
+  static constexpr int V_IPW = (V_INS + NW - 1) / NW;
+  static constexpr int KB = BC / 32;                   // 32-key blocks per tile
+  static constexpr int KS = D / 16;                    // k-steps of QK^T
+  static constexpr int DT = D / 32;                    // 32-wide d tiles of O
+  static constexpr int PT = BC / 16;                   // 16-key chunks (PV k-steps)
+  static constexpr int NQ = KS * KB;                   // QK^T MFMAs per tile
+  static constexpr int NP = PT * DT;                   // PV MFMAs per tile
+  static constexpr int NPAIR = PT * 4;                 // pairs of exponentials per tile
+  static constexpr int P1 = (NPAIR * 5) / 8;           // pairs done in phase 1
+  static constexpr int NE = NP / 2;                    // phase-2 steps that do exponentials
+  static constexpr int PF = 2;                         // LDS read-ahead, in steps
+  static_assert((NPAIR - P1) <= NE * 2, "phase 2 must finish the exponentials");
+
+  using T = typename E::T;
+  using V8 = typename E::V8;
+  using V4 = typename E::V4;
+  using V2 = typename E::V2;
+  using Scores = f32x16[KB];
+
+  struct State {
+    int lane, wave, hl, l32;
+    int q_w0;                   // first query row of this wave
+    int kv_limit;               // keys >= kv_limit are excluded
+    int n_act;                  // tiles with keys for this work-group
+    const char* kp;             // K / V of this (batch, kv-head), key 0
+    const char* vp;
+    int64_t k_tile, v_tile;     // bytes between consecutive tiles
+    int64_t k_end, v_end;       // bytes from kp / vp to the end of key Nk-1
+    uint32_t koff[K_IPW], voff[V_IPW];  // per load instruction: byte offset in a tile
+    int kbase, vbase;           // per-lane LDS byte offsets of the read patterns
+    float c;                    // scale * log2(e)
+    V8 qf[KS];                  // Q fragments (B operand of S^T = K Q^T)
+    f32x16 acc[DT];             // O^T accumulators
+    float m_run, l_run;
+  };
+
+  // Byte offset, within a tile of row pitch sn elements, of the 16-byte
+  // chunk lane `lane` copies in load instruction `ins` of a tile with `ps`
+  // LDS slots per row; pad slots and columns past d get an out-of-range
+  // offset (the load returns zero).
+  static __device__ __forceinline__ uint32_t dma_offset(int ins, int lane, int ps, int dchunks,
+                                                        int64_t sn) {
+    const int s = ins * 64 + lane;
+    const int r = s / ps, ch = s % ps;
+    if (r >= BC || ch >= dchunks) return kBufOutOfRange;
+    return (uint32_t)((r * sn + ch * 8) * 2);
+  }
+
+  static __device__ __forceinline__ void issue_k(const State& st, int j, char* kb) {
+    const int64_t ko = (int64_t)j * st.k_tile;
+    const BufRsrc rk = make_rsrc(st.kp + ko, (uint32_t)min(st.k_end - ko, (int64_t)kBufLimit));
+#pragma unroll
+    for (int i = 0; i < K_IPW; ++i) {
+      const int ins = i * NW + st.wave;
+      if (ins < K_INS) dma16_buf(rk, st.koff[i], kb + ins * 1024);
+    }
+  }
+  static __device__ __forceinline__ void issue_v(const State& st, int j, char* vb) {
+    const int64_t vo = (int64_t)j * st.v_tile;
+    const BufRsrc rv = make_rsrc(st.vp + vo, (uint32_t)min(st.v_end - vo, (int64_t)kBufLimit));
+#pragma unroll
+    for (int i = 0; i < V_IPW; ++i) {
+      const int ins = i * NW + st.wave;
+      if (ins < V_INS) dma16_buf(rv, st.voff[i], vb + ins * 1024);
+    }
+  }
+
+  static __device__ __forceinline__ const char* kaddr(const State& st, const char* kbuf, int i) {
+    return kbuf + st.kbase + (i % KB) * 32 * KP + (i / KB) * 32;
+  }
+
+  static __device__ __forceinline__ void qk_plain(const State& st, const char* kbuf, Scores& s) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) s[k] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+      s[i % KB] = E::mfma(lds_read16<V8>(kaddr(st, kbuf, i)), st.qf[i / KB], s[i % KB]);
+  }
+
+  static __device__ __forceinline__ bool is_edge(const State& st, int j) {
+    return j * BC + BC > st.kv_limit;
+  }
+  static __device__ __forceinline__ void mask_edge(const State& st, Scores& s, int j) {
+    const int j0 = j * BC;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = j0 + k * 32 + (e >> 2) * 8 + st.hl * 4 + (e & 3);
+        if (key >= st.kv_limit) s[k][e] = -INFINITY;
+      }
+  }
+  static __device__ __forceinline__ float row_max(const Scores& s) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[k][e]);
+    return max_with_other_half(mx);
+  }
+  // Lazy rescale given a tile's row maximum mx (raw score units).
+  static __device__ __forceinline__ void rescale(State& st, float mx) {
+    const float cand = mx * st.c;
+    if (__builtin_amdgcn_ballot_w64(cand > st.m_run + TH)) {
+      const float m_new = fmaxf(st.m_run, cand);
+      if (m_new > st.m_run) {
+        const float alpha = (st.m_run == -INFINITY) ? 0.f : fast_exp2(st.m_run - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+        st.m_run = m_new;
+      }
+    }
+  }
+
+  // Main block of iteration j: exponentials and PV of tile j (scores sc, V
+  // tile vc) with S of tile j+1 (into sn, from K tile kn).  Returns this
+  // lane's share of tile j+1's unmasked row maximum.
+  static __device__ __forceinline__ float main_block(State& st, const Scores& sc, Scores& sn,
+                                                     const char* kn, const char* vc) {
+    const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
+    float lsum = 0.f;
+    V2 pp[NPAIR];
+    V8 kf[NQ];
+    V8 vf[NP];
+    auto vload = [&](int i) {
+      const char* p = vc + st.vbase + (i / DT) * 16 * VP + (i % DT) * 64;
+      const V4 lo = lds_read_tr4<V4>(p);
+      const V4 hi = lds_read_tr4<V4>(p + 8 * VP);
+      vf[i] = concat4<V8, V4>(lo, hi);
+    };
+    // pair p: elements 2q, 2q+1 of 16-key chunk t = p / 4 (slot order of the
+    // P operand, see FwdKernel)
+    auto pair = [&](int p) {
+      const int t = p / 4, q = p % 4, k = t >> 1, e = (t & 1) * 8 + 2 * q;
+      const float x0 = fast_exp2(__builtin_fmaf(sc[k][e], st.c, -mref));
+      const float x1 = fast_exp2(__builtin_fmaf(sc[k][e + 1], st.c, -mref));
+      lsum += x0 + x1;  // fp32 sum of the unrounded p
+      pp[p] = E::cvt2(x0, x1);
+      asm volatile("" : "+v"(lsum));
+      asm volatile("" : "+v"(pp[p]));
+    };
+    auto pfrag = [&](int t) {
+      const V4 lo = __builtin_shufflevector(pp[4 * t], pp[4 * t + 1], 0, 1, 2, 3);
+      const V4 hi = __builtin_shufflevector(pp[4 * t + 2], pp[4 * t + 3], 0, 1, 2, 3);
+      return concat4<V8, V4>(lo, hi);
+    };
+
+#pragma unroll
+    for (int k = 0; k < KB; ++k) sn[k] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = lds_read16<V8>(kaddr(st, kn, i));
+    // phase 1
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      if (i + PF < NQ) kf[i + PF] = lds_read16<V8>(kaddr(st, kn, i + PF));
+      else vload(i + PF - NQ);
+      sn[i % KB] = E::mfma(kf[i], st.qf[i / KB], sn[i % KB]);
+#pragma unroll
+      for (int p = (i * P1) / NQ; p < ((i + 1) * P1) / NQ; ++p) pair(p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase 2
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i + PF < NP) vload(i + PF);
+      st.acc[i % DT] = E::mfma(vf[i], pfrag(i / DT), st.acc[i % DT]);
+      if (i < NE) {
+#pragma unroll
+        for (int p = P1 + (i * (NPAIR - P1)) / NE; p < P1 + ((i + 1) * (NPAIR - P1)) / NE; ++p)
+          pair(p);
+      } else {
+        constexpr int NM = NP - NE, NV = KB * 16;
+#pragma unroll
+        for (int e = ((i - NE) * NV) / NM; e < ((i - NE + 1) * NV) / NM; ++e)
+          mx = fmaxf(mx, sn[e / 16][e % 16]);
+        asm volatile("" : "+v"(mx));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st.l_run += lsum;
+    return mx;
+  }
+
+  // Top of iteration j: K(j+1) and V(j) (issued one iteration ago) have
+  // landed for every wave once all pass the barrier; then K(j+2) and V(j+1)
+  // go into the buffers iteration j-1 has finished with.
+  static __device__ __forceinline__ void sync_and_issue(const State& st, int j, int n,
+                                                        char* kdst, char* vdst) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < n) issue_v(st, j + 1, vdst);
+    if (j + 2 < n) issue_k(st, j + 2, kdst);
+  }
+
+  // After the main block of iteration j: tile j+1's maximum and rescale.
+  static __device__ __forceinline__ void finish_next(State& st, Scores& sn, int j, float mx) {
+    if (j + 1 < st.n_act) {
+      if (is_edge(st, j + 1)) {
+        mask_edge(st, sn, j + 1);
+        mx = row_max(sn);
+      } else {
+        mx = max_with_other_half(mx);
+      }
+      rescale(st, mx);
+    }
+  }
+
+  static __device__ __forceinline__ void run(const FwdArgs& a, char* k0, char* v0, char* k1,
+                                             char* v1) {
+    State st;
+    st.lane = threadIdx.x & 63;
+    st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    st.hl = st.lane >> 5;
+    st.l32 = st.lane & 31;
+
+    const int wid = xcd_remap(blockIdx.x, a.total_blocks);
+    const int qblk = wid % a.nqb;
+    const int bh = wid / a.nqb;
+    const int h = bh % a.Hq;
+    const int b = bh / a.Hq;
+    const int g = h / a.group;
+    st.q_w0 = qblk * ROWS + st.wave * 32;
+
+    st.kv_limit = a.Nk;
+    if (a.kv_lens) st.kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
+    st.n_act = (st.kv_limit + BC - 1) / BC;
+    const int n_tiles = st.n_act;
+    const int dchunks = a.d / 8;
+    st.c = a.c;
+    st.kp = (const char*)((const T*)a.k + b * a.k_sb + g * a.k_sh);
+    st.vp = (const char*)((const T*)a.v + b * a.v_sb + g * a.v_sh);
+    st.k_tile = (int64_t)BC * a.k_sn * 2;
+    st.v_tile = (int64_t)BC * a.v_sn * 2;
+    st.k_end = ((int64_t)(a.Nk - 1) * a.k_sn + a.d) * 2;
+    st.v_end = ((int64_t)(a.Nk - 1) * a.v_sn + a.d) * 2;
+#pragma unroll
+    for (int i = 0; i < K_IPW; ++i)
+      st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn);
+#pragma unroll
+    for (int i = 0; i < V_IPW; ++i)
+      st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn);
+    // K read: lane holds key row l32 (+32 k), chunk 2 ks + hl.
+    st.kbase = st.l32 * KP + st.hl * 16;
+    // V transposed read: in each 16-lane group lane i points at row
+    // 4 (group / 2) + i / 4 (+16 t, +8), column 16 (group % 2) + 4 (i % 4)
+    // (+32 dt), so that lane l gets column l of four consecutive rows.
+    {
+      const int grp = st.lane >> 4, gi = st.lane & 15;
+      st.vbase = (4 * (grp >> 1) + (gi >> 2)) * VP + (16 * (grp & 1) + 4 * (gi & 3)) * 2;
+    }
+
+    const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh;
+    {
+      const int row = min(st.q_w0 + st.l32, a.Nq - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 16 + st.hl * 8;
+        st.qf[ks] = d0 < a.d ? *(const V8*)(qp + row * a.q_sn + d0) : V8{};
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    Scores s0, s1;
+    if (n_tiles > 0) {
+      // tile j: K in k[j%2], V in v[j%2]
+      issue_k(st, 0, k0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      qk_plain(st, k0, s0);
+      if (is_edge(st, 0)) mask_edge(st, s0, 0);
+      rescale(st, row_max(s0));
+      issue_v(st, 0, v0);
+      if (1 < n_tiles) issue_k(st, 1, k1);
+      // Every iteration also computes S of the following tile; after the
+      // last tile that result is not used (the K buffer then holds stale
+      // data, which is harmless).
+      for (int j = 0; j < n_tiles; j += 2) {
+        sync_and_issue(st, j, n_tiles, k0, v1);
+        finish_next(st, s1, j, main_block(st, s0, s1, k1, v0));
+        if (j + 1 >= n_tiles) break;
+        sync_and_issue(st, j + 1, n_tiles, k1, v0);
+        finish_next(st, s0, j + 1, main_block(st, s1, s0, k0, v1));
+      }
+    }
+
+    // Epilogue: O /= l, LSE = ln2 (m + log2 l).
+    T* op = (T*)a.o + b * a.o_sb + h * a.o_sh;
+    const float l_tot = add_with_other_half(st.l_run);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const int row = st.q_w0 + st.l32;
+    if (row < a.Nq) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = dt * 32 + gq * 8 + st.hl * 4;
+          if (col < a.d) {
+            auto lo = E::cvt2(st.acc[dt][gq * 4 + 0] * inv, st.acc[dt][gq * 4 + 1] * inv);
+            auto hi = E::cvt2(st.acc[dt][gq * 4 + 2] * inv, st.acc[dt][gq * 4 + 3] * inv);
+            V4 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+            *(V4*)(op + row * a.o_sn + col) = w;
+          }
+        }
+      }
+      if (st.hl == 0)
+        a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] =
+            l_tot > 0.f ? (st.m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+};
+
+template <class E, int D, int BC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pipe_kernel(FwdArgs a) {
+  using K = FwdPipeKernel<E, D, BC>;
+  __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[K::V_BYTES];
+  K::run(a, k0, v0, k1, v1);
+}
+
+}  // namespace attn

@@ -97,6 +97,24 @@ __device__ __forceinline__ void dma16(const void* gsrc, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (LDS_AS void*)lds_wave_base, 16, 0, 0);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets at or past
+// `bytes` return zero instead of touching memory.  The last descriptor word
+// selects a raw buffer with 32-bit data format (gfx9 family encoding).
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Same as dma16, through a buffer resource: the lane's 16 bytes at byte
+// offset voff (zero if out of range) land at lds_wave_base + 16 * lane.
+__device__ __forceinline__ void dma16_buf(BufRsrc r, uint32_t voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+// Offset that is out of range of every resource built by make_rsrc with
+// bytes <= kBufLimit.
+constexpr uint32_t kBufLimit = 0x7fffffffu;
+constexpr uint32_t kBufOutOfRange = 0x80000000u;
+
 // Value of x held by lane l ^ 32, combined with x by max / add.
 __device__ __forceinline__ float max_with_other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -40,7 +40,7 @@ def make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed, std=1.0, lens=None, with_do=Fa
 
 
 def check_out(o_gpu, lse_gpu, O_ref, L_ref, dtype, label=""):
-    """Element-wise comparison of O and LSE with the oracle (the benchmark spec bar)."""
+    """Element-wise comparison of O and LSE with the oracle (max-abs bar of the tolerance table)."""
     O = host(o_gpu)
     L = host(lse_gpu)
     assert O.shape == O_ref.shape, (O.shape, O_ref.shape)

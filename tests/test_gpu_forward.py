@@ -58,6 +58,12 @@ SMALL = [
     ("bf16_large_logits", 1, 2, 2, 200, 500, 128, "bf16", False, None, None, "bhnd", 2.0, 1.0),
     ("fp16_dead_rows_mask", 1, 1, 1, 64, 64, 64, "fp16", False, None, "dead_rows", "bhnd", None, 1.0),
     ("bf16_lens_zero", 3, 2, 2, 70, 90, 64, "bf16", False, (0, 2), None, "bhnd", None, 1.0),
+    # >= 8 key tiles without masks: the software-pipelined kernel
+    ("bf16_d128_pipe_ragged_gqa", 1, 2, 1, 300, 700, 128, "bf16", False, None, None, "bhnd", None, 1.0),
+    ("fp16_d64_pipe_lens_mid_tile", 2, 2, 2, 129, 600, 64, "fp16", False, (530, 600), None, "bhnd", None, 1.0),
+    ("bf16_d40_pipe_bnhd_tail", 1, 3, 3, 70, 515, 40, "bf16", False, None, None, "bnhd", None, 1.0),
+    ("fp16_d128_pipe_large_logits", 1, 2, 2, 64, 1030, 128, "fp16", False, None, None, "bhnd", 2.0, 1.0),
+    ("bf16_d128_pipe_one_tile", 2, 1, 1, 40, 520, 128, "bf16", False, (3, 64), None, "bhnd", None, 1.0),
 ]
 
 
@@ -109,10 +115,11 @@ def test_forward_empty_and_no_keys(gpu_lib):
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
 
-def test_forward_is_deterministic_and_layout_invariant(gpu_lib):
+@pytest.mark.parametrize("nk", [333, 600])
+def test_forward_is_deterministic_and_layout_invariant(gpu_lib, nk):
     import torch
-    _say("[fwd] determinism / layouts")
-    w, x = make_case(2, 4, 2, 333, 333, 128, "bf16", seed=77)
+    _say(f"[fwd] determinism / layouts nk={nk}")
+    w, x = make_case(2, 4, 2, 333, nk, 128, "bf16", seed=77)
     o1, l1 = _run(w, x)
     o2, l2 = _run(w, x)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
