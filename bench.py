@@ -37,8 +37,20 @@ METRIC = "attention fwd TFLOPS & % of bf16 MFMA peak at B8 H32 N4096 d128"
 DEFAULT_WORKLOAD = "long_bf16_b8_h32_n4096_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_bf16_b8_h32_n4096_d128_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_25_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "attn_fwd_kernel.h", "device_common.h",
-                            "attn_kernels.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_kernel.h", "attn_fwd_pipe_kernel.h",
+                            "device_common.h", "attn_kernels.h")]
+
+
+def fwd_kernel_name(w) -> str:
+    """The forward kernel instance attn_fwd dispatches to for workload w
+    (mirrors the dispatch in attn_fwd.hip)."""
+    D = 128 if w.d > 64 else 64
+    if w.dtype == "fp32":
+        return f"attn::fwd32_kernel<{D},...>"
+    e = "BF16" if w.dtype == "bf16" else "FP16"
+    if not w.causal and w.Nk >= 8 * 64:
+        return f"attn::fwd_pipe_kernel<{e},{D},64>"
+    return f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal).lower()},mask=false>"
 
 
 def kernel_source_hash() -> str:
@@ -269,7 +281,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": None if bwd else recorded_traffic(),
                      "kernel": ("attn::bwd_q_kernel + attn::bwd_kv_kernel (+ reduce), one call per step"
-                                if bwd else "attn::fwd_kernel<BF16,128,8,64> (one launch per step)")},
+                                if bwd else fwd_kernel_name(w) + " (one launch per step)")},
     }
     if args.extras:
         print("[bench] extras", file=sys.stderr, flush=True)
