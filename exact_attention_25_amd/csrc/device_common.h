@@ -137,6 +137,22 @@ __device__ __forceinline__ int xcd_remap(int hw_id, int total) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Work-group id -> (rank, combo) for a grid of n_combo x n_rank work-groups:
+// when n_combo is a multiple of 8, each XCD takes its own n_combo/8 combos
+// and, within the XCD, work-groups start in rank order (rank 0 first);
+// otherwise ranks go in order over the whole grid.  Giving the heaviest
+// work-groups the lowest ranks schedules them first.
+__device__ __forceinline__ void rank_combo(int hw_id, int n_combo, int& rank, int& combo) {
+  if (n_combo % 8 == 0) {
+    const int cpx = n_combo / 8, xcd = hw_id % 8, idx = hw_id / 8;
+    rank = idx / cpx;
+    combo = xcd * cpx + idx % cpx;
+  } else {
+    rank = hw_id / n_combo;
+    combo = hw_id % n_combo;
+  }
+}
+
 // LDS swizzles for a row-major tile of rows of CPR 16-byte chunks.
 // K-type tiles are read 16 rows x one chunk at a time (ds_read_b128): the XOR
 // spreads 16 consecutive rows over distinct chunk slots of a 256-byte window.
