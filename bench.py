@@ -36,6 +36,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPS & % of bf16 MFMA peak at B8 H32 N4096 d128"
 DEFAULT_WORKLOAD = "long_bf16_b8_h32_n4096_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_bf16_b8_h32_n4096_d128_traffic.txt")
+# Workloads whose floor is HBM bandwidth (or launch latency) rather than MFMA
+HBM_BOUND = ("vit_bf16_b128_h16_n196_d64", "unet_cross_fp16_b2_h8_q4096_k77_d40")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_25_amd", "csrc", f)
                   for f in ("attn_fwd.hip", "attn_fwd_kernel.h", "attn_fwd_pipe_kernel.h",
                             "device_common.h", "attn_kernels.h")]
@@ -97,6 +99,32 @@ def time_calls(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def call_percentiles(fn, n, stream):
+    """Per-call durations (ms) of n further calls, each bracketed by its own
+    HIP events on the launch stream: p10, p50, p90."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+    return {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4), "calls": n}
+
+
+def rotating_sets(t, w, min_bytes):
+    """Copies of the inputs (and the outputs' room) so that cycling through
+    them touches at least min_bytes of HBM: with a working set above the
+    256 MB last-level cache every call reads its inputs from HBM."""
+    # q, k, v read and o (the size of q) written per call
+    per_set = sum(t[n].numel() * t[n].element_size() for n in ("q", "k", "v", "q"))
+    n = max(2, min(256, -(-min_bytes // per_set)))
+    return [{k: (v.clone() if v is not None else None) for k, v in t.items()} for _ in range(n)]
 
 
 def workload_inputs(w, device, with_do=False):
@@ -175,6 +203,22 @@ def run_extras(device, steps, warmup):
                "fwd_pct_peak": round(fl / ms / 1e9 / acc.PEAK_TFLOPS[w.dtype] * 100, 2),
                "fwd_min_bytes_gbs": round(by / ms / 1e6, 1),
                "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1)}
+        if w.name in HBM_BOUND:
+            # inputs rotated through >= 768 MB so that they come from HBM, not
+            # from the last-level cache
+            sets = rotating_sets(t, w, 768 << 20)
+            it = [0]
+
+            def rfn():
+                u = sets[it[0] % len(sets)]
+                it[0] += 1
+                return bd.attn_fwd(u["q"], u["k"], u["v"], causal=w.causal, kv_lens=u["kv_lens"])
+            rms, _ = time_calls(rfn, max(steps, 2 * len(sets)), len(sets), stream)
+            rec.update({"fwd_ms_rotated": round(rms, 4),
+                        "fwd_min_bytes_gbs_rotated": round(by / rms / 1e6, 1),
+                        "rotated_sets": len(sets),
+                        "fwd_pct_hbm_peak_rotated": round(by / rms / 1e6 / acc.PEAK_HBM_GBS * 100, 1)})
+            del sets
         if w.backward:
             o, lse = fn()
             bfn = lambda: bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal,
@@ -201,6 +245,9 @@ def main():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="override the workload's batch size (counter runs whose per-dispatch "
+                         "cycle counts must stay below 2^31); the JSON line then names the new B")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward from the forward's O/LSE")
     args = ap.parse_args()
@@ -228,6 +275,9 @@ def main():
         if not m:
             raise SystemExit(f"unknown workload {args.workload}")
         w = inputs.sweep_workload(int(m.group(1)))
+    if args.batch > 0 and args.batch != w.B:
+        import dataclasses
+        w = dataclasses.replace(w, B=args.batch, name=re.sub(r"_b\d+_", f"_b{args.batch}_", w.name, 1))
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     bwd = args.which == "bwd"
     x, t = workload_inputs(w, device, with_do=bwd)
@@ -257,6 +307,8 @@ def main():
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     ms, wall = time_calls(fn, args.steps, args.warmup, stream)
 
+    pct = call_percentiles(fn, min(args.steps, 50), stream)
+
     tflops = flops / ms / 1e9
     peak = acc.PEAK_TFLOPS[w.dtype]
     rec = {
@@ -267,6 +319,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_call_percentiles": pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
