@@ -333,7 +333,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": None if bwd else recorded_traffic(),
-                     "kernel": ("attn::bwd_q_kernel + attn::bwd_kv_kernel (+ reduce), one call per step"
+                     "kernel": ("attn::bwd_prep_kernel + attn::bwd_q_kernel + attn::bwd_kv_kernel (+ reduce), one call per step"
                                 if bwd else fwd_kernel_name(w) + " (one launch per step)")},
     }
     if args.extras:

@@ -93,19 +93,24 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: D [B,Hq,ld] | nl2 [B,Hq,ld] | (kv_chunks > 1) partial
-// dK and dV, [kv_chunks, B, Hkv, Nk, d] fp32 each; ld = Nq rounded up to 64.
+// dK and dV, [kv_chunks, B, Hkv, Nk, d] fp32 each | (bf16 inputs) fp16
+// copies of q, dout and k in their own layout; ld = Nq rounded up to 128.
 struct BwdWorkspace {
-  size_t rows, part, total;
+  size_t rows, part, cq, ck, total;
   int chunks, ld;
 };
 
 BwdWorkspace bwd_workspace(const attn_params* p) {
   BwdWorkspace w;
   w.chunks = attn::bwd_kv_chunks(p->B, p->Hkv, p->Nk, p->Hq / p->Hkv);
-  w.ld = (p->Nq + 63) / 64 * 64;
+  w.ld = (p->Nq + 127) / 128 * 128;
   w.rows = align256((size_t)p->B * p->Hq * w.ld * sizeof(float));
   w.part = w.chunks > 1 ? align256((size_t)w.chunks * p->B * p->Hkv * p->Nk * p->d * sizeof(float)) : 0;
-  w.total = 2 * w.rows + 2 * w.part;
+  // bf16 inputs: fp16 copies of q and dout (cq bytes each) and of k (ck)
+  const bool cvt = p->dtype == ATTN_BF16;
+  w.cq = cvt ? align256((size_t)p->B * p->Hq * p->Nq * p->d * 2) : 0;
+  w.ck = cvt ? align256((size_t)p->B * p->Hkv * p->Nk * p->d * 2) : 0;
+  w.total = 2 * w.rows + 2 * w.part + 2 * w.cq + w.ck;
   return w;
 }
 
@@ -143,6 +148,16 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.nl2 = reinterpret_cast<float*>(wsp + ws.rows);
   a.part_dk = ws.part ? reinterpret_cast<float*>(wsp + 2 * ws.rows) : nullptr;
   a.part_dv = ws.part ? reinterpret_cast<float*>(wsp + 2 * ws.rows + ws.part) : nullptr;
+  if (ws.cq) {
+    char* c = wsp + 2 * ws.rows + 2 * ws.part;
+    a.q16 = c;
+    a.do16 = c + ws.cq;
+    a.k16 = c + 2 * ws.cq;
+  } else {
+    a.q16 = q;
+    a.do16 = dout;
+    a.k16 = k;
+  }
   a.kv_chunks = ws.chunks;
   a.ld_rows = ws.ld;
   a.kv_lens = p->kv_lens;

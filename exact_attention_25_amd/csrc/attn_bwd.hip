@@ -1,5 +1,7 @@
 // Backward attention: kernel instances, work split and dispatch (the kernels
 // are in attn_bwd_kernel.h).
+#include <type_traits>
+
 #include "attn_bwd_kernel.h"
 
 namespace attn {
@@ -15,10 +17,39 @@ int bwd_kv_chunks(int B, int Hkv, int Nk, int group) {
   return group;
 }
 
+// bf16 -> fp16 copies of q, dout (n16q elements each) and k (n16k), 8
+// elements per 16-byte access (the element counts are multiples of 8).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int64_t n8q, int64_t n8k) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n8q + n8k; i += stride) {
+    const bf16x8* src;
+    f16x8* dst;
+    int64_t j = i;
+    if (j < n8q) {
+      src = (const bf16x8*)a.q; dst = (f16x8*)a.q16;
+    } else if ((j -= n8q) < n8q) {
+      src = (const bf16x8*)a.dout; dst = (f16x8*)a.do16;
+    } else {
+      j -= n8q;
+      src = (const bf16x8*)a.k; dst = (f16x8*)a.k16;
+    }
+    dst[j] = to_f16x8<BF16>(src[j]);
+  }
+}
+
 template <class E, int D>
 static hipError_t launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
-  constexpr int NW_KV = kBwdKeysPerBlock / 32, BR = 64;
-  constexpr int NW_Q = 4, BC = 64;
+  constexpr int NW_KV = kBwdKeysPerBlock / 32, BR = 128;
+  constexpr int NW_Q = 4, BC = 128;
+  if (std::is_same<E, BF16>::value) {
+    const int64_t n8q = (int64_t)a.B * a.Hq * a.Nq * a.d / 8;
+    const int64_t n8k = (int64_t)a.B * a.Hkv * a.Nk * a.d / 8;
+    const int64_t n = 2 * n8q + n8k;
+    if (n > 0) {
+      const int blocks = (int)((n + 255) / 256 < 16384 ? (n + 255) / 256 : 16384);
+      hipLaunchKernelGGL(bwd_prep_kernel, dim3(blocks), dim3(256), 0, st, a, n8q, n8k);
+    }
+  }
   // dQ, and D / nl2 per row for the dK/dV pass
   if (a.Nq > 0) {
     const int nqb = (a.Nq + NW_Q * 32 - 1) / (NW_Q * 32);

@@ -18,25 +18,38 @@
 // grouped-query sums need no atomics).
 //
 // Precision: the matrix products that take P or dS as an operand use fp16
-// (11-bit significand) rather than bf16; bf16 inputs are converted to fp16
-// for those products (exact for |x| in [2^-14, 65504]).  Exponentials are
-// exp2 with the scale and log2(e) folded in: P = exp2(s * c + nl2), with
-// nl2 = -LSE * log2(e) (-inf for a fully masked row and for the padding rows
-// past Nq, so that P = 0 there without further masking).
+// (11-bit significand) rather than bf16.  For bf16 inputs a first pass
+// (bwd_prep_kernel) writes fp16 copies of Q, dO and K (exact for |x| in
+// [2^-14, 65504]); the tiles of those copies then go to LDS unchanged.
+// Exponentials are exp2 with the scale and log2(e) folded in:
+// P = exp2(s * c + nl2), with nl2 = -LSE * log2(e) (-inf for a fully masked
+// row and for the padding rows past Nq, so that P = 0 there).
 //
-// Tiles stream through LDS with a padded row pitch of D/8 + 1 16-byte slots,
-// filled by direct buffer->LDS loads (rows or columns past the tensor read as
-// zero).  Row-fragment reads (16 rows x one 16-byte chunk per 16 lanes) are
+// Tiles of 128 rows (dK/dV) or keys (dQ) stream through LDS, double-
+// buffered, with a padded row pitch of D/8 + 1 16-byte slots, filled by
+// direct buffer->LDS loads (rows or columns past the tensor read as zero).
+// Row-fragment reads (16 rows x one 16-byte chunk per 16 lanes) are
 // conflict-free; transposed reads (4 rows x 64 bytes per half-wave) share
 // banks pairwise.  Every read address is a per-lane base plus a compile-time
-// offset.  Causal and key-length masking is applied only to tiles that
-// cross a boundary.
+// offset.
+//
+// Both kernels run a tile as a fixed software pipeline over its four 32-row
+// (32-key) sub-blocks, one wave per SIMD: the S/dP products of sub-block i
+// are issued while the dV/dK (A/B) products of sub-block i-1 run beside the
+// exponentials of sub-block i, and each LDS operand is read PF products
+// ahead.  Masking costs no per-element work in the loop: the S accumulator
+// of a sub-block starts at -inf where a key is excluded (causal, and in the
+// dQ kernel also keys past kv_lens), 0 elsewhere, so P = 0 and dS = 0 there.
+// The dK/dV kernel leaves keys past kv_lens unmasked: their P and dS reach
+// only their own rows of dK and dV, which it stores as zero.
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "attn_kernels.h"
 #include "device_common.h"
+
 
 namespace attn {
 
@@ -78,21 +91,6 @@ struct PadTile {
       if (ins < INS) dma16_buf(rs, off[i], buf + ins * 1024);
     }
   }
-  // In-place bf16 -> fp16 conversion of the slots this lane loaded (after its
-  // own loads have landed; identity for fp16 inputs).
-  template <class E>
-  static __device__ __forceinline__ void to_f16(char* buf, int wave, int lane) {
-    if constexpr (!std::is_same<E, FP16>::value) {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int ins = i * NW + wave;
-        if (ins < INS) {
-          char* p = buf + ins * 1024 + lane * 16;
-          *(LDS_AS f16x8*)(LDS_AS void*)(p) = to_f16x8<E>(lds_read16<typename E::V8>(p));
-        }
-      }
-    }
-  }
   // Lane bases: row fragment (row l32, chunk hl) and transposed read (row
   // 4 (group / 2) + i / 4, column 16 (group % 2) + 4 (i % 4) for lane i of
   // 16-lane group `group`).
@@ -120,8 +118,8 @@ struct PadTile {
 // --------------------------------------------------------------- dQ kernel
 // One work-group of NW waves per (batch, q-head, block of NW*32 rows); each
 // wave owns 32 rows, whose Q (as fp16) and dO fragments stay in registers.
-// K and V tiles of BC keys stream through LDS (K converted to fp16 there).
-// Per tile and wave:
+// Tiles of BC keys of K (its fp16 copy) and V stream through LDS.  Per
+// 32-key block of a tile and wave:
 //   S^T = K Q^T, dP^T = V dO^T        32x32x16 MFMA; each lane holds 16 keys
 //                                     of one row
 //   P^T, X^T = P^T * dP^T, D += X     per element
@@ -135,7 +133,7 @@ struct BwdQ {
   static constexpr int KB = BC / 32;
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int PT = BC / 16;
+  static constexpr int PF = 3;                // LDS operand read-ahead, in MFMAs
 
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -164,72 +162,158 @@ struct BwdQ {
     TL::load(make_rsrc(st.vp + o, n), st.off, vb, st.wave);
   }
 
-  template <bool EDGE>
-  static __device__ __forceinline__ void tile(State& st, const char* kc, const char* vc, int j0) {
-    f32x16 s[KB], dp[KB];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      s[k] = f32x16{};
-      dp[k] = f32x16{};
+  // ---- software-pipelined tile: blocks of MFMAs per 32-key block k ----
+  //   SD(0) | p/x(0) | SD(1) | GR(0)+p/x(1) | ... | SD(KB-1) | GR(KB-2)+p/x(KB-1) | GR(KB-1)
+  // SD(k): the 2 KS S^T / dP^T MFMAs of key block k; GR(k): its 4 DT A^T /
+  // B^T MFMAs (each transposed K^T fragment feeds one A^T and one B^T MFMA);
+  // 16 each at d = 128.
+  static constexpr int NBLK = 2 * KB + 1;
+  static constexpr int SDN = 2 * KS;   // MFMAs of an SD block
+  static constexpr int GRN = 4 * DT;   // MFMAs of a GR block
+  static __host__ __device__ constexpr int blk_len(int b) {
+    return (b % 2 == 0) ? (b / 2 < KB ? SDN : GRN) : (b == 1 ? 0 : GRN);
+  }
+  static __host__ __device__ constexpr int blk_start(int b) {
+    int s = 0;
+    for (int q = 0; q < b; ++q) s += blk_len(q);
+    return s;
+  }
+  static constexpr int NSLOT = KB * (SDN + GRN);
+  static __host__ __device__ constexpr int slot_blk(int s) {
+    int b = 0;
+    for (int q = 0; q < NBLK; ++q)
+      if (blk_len(q) > 0 && blk_start(q) <= s) b = q;
+    return b;
+  }
+  static __host__ __device__ constexpr int slot_kind(int s) {
+    const int b = slot_blk(s);
+    return (b % 2 == 0 && b / 2 < KB) ? 0 : 1;
+  }
+  static __host__ __device__ constexpr int slot_sub(int s) {
+    const int b = slot_blk(s);
+    return slot_kind(s) == 0 ? b / 2 : (b % 2 == 1 ? (b - 1) / 2 - 1 : KB - 1);
+  }
+  static __host__ __device__ constexpr int slot_m(int s) { return s - blk_start(slot_blk(s)); }
+  static __host__ __device__ constexpr int group_slot(int k, int g) {
+    return k == 0 ? blk_start(2) : blk_start(2 * k + 1) + g * (GRN / 4);
+  }
+  // does slot s read an LDS operand (transposed K^T fragments are read once
+  // for a pair of MFMAs)
+  static __host__ __device__ constexpr bool slot_reads(int s) {
+    return slot_kind(s) == 0 || (slot_m(s) & 1) == 0;
+  }
+
+  struct Pipe {
+    const char* kc;
+    const char* vc;
+    int lim;                    // keys with offset > lim are masked (see pipe_slot)
+    f32x16 s, dp;
+    H8 pf[2][2], xf[2][2];
+    H8 opd[NSLOT];
+    V8 opv[NSLOT];
+  };
+  template <int SL>
+  static __device__ __forceinline__ void pipe_load(const State& st, Pipe& c) {
+    if constexpr (SL < NSLOT && slot_reads(SL)) {
+      constexpr int k = slot_sub(SL), m = slot_m(SL);
+      if constexpr (slot_kind(SL) == 0) {
+        if constexpr (m & 1) c.opv[SL] = TL::template row<V8>(c.vc, st.rb, k * 32, m >> 1);
+        else c.opd[SL] = TL::template row<H8>(c.kc, st.rb, k * 32, m >> 1);
+      } else {
+        c.opd[SL] = TL::template tr<H8, H4>(c.kc, st.tb, k * 32 + (m / (2 * DT)) * 16, (m >> 1) % DT);
+      }
     }
+  }
+  template <int K, int GQ>
+  static __device__ __forceinline__ void pipe_group(State& st, Pipe& c) {
+    constexpr int par = K & 1;
+    float pv[4], xv[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        s[k] = FP16::mfma(TL::template row<H8>(kc, st.rb, k * 32, ks), st.qf[ks], s[k]);
-        dp[k] = E::mfma(TL::template row<V8>(vc, st.rb, k * 32, ks), st.df[ks], dp[k]);
-      }
-    H8 pf[PT], xf[PT];
-#pragma unroll
-    for (int t = 0; t < PT; ++t) {
-      const int k = t >> 1, r0 = (t & 1) * 8;
-      float pv[8], xv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = r0 + e;
-        float p = fast_exp2(__builtin_fmaf(s[k][r], st.c, st.nl2));
-        if constexpr (EDGE) {
-          const int key = j0 + k * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
-          const bool vis = key < st.kv_limit && (!CAUSAL || key <= st.qrow);
-          p = vis ? p : 0.f;
-        }
-        pv[e] = p;
-        xv[e] = p * dp[k][r];
-        st.dsum[e & 3] += xv[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const f16x2 p2 = FP16::cvt2(pv[e], pv[e + 1]);
-        const f16x2 x2 = FP16::cvt2(xv[e], xv[e + 1]);
-        pf[t][e] = p2[0];
-        pf[t][e + 1] = p2[1];
-        xf[t][e] = x2[0];
-        xf[t][e + 1] = x2[1];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, st.nl2));
+      pv[e] = p;
+      xv[e] = p * c.dp[GQ * 4 + e];
+      st.dsum[e] += xv[e];
     }
-    // A^T += K^T X^T, B^T += K^T P^T (K^T read transposed from the tile)
+    constexpr int t2 = GQ >> 1, half = (GQ & 1) * 4;
+    const f16x2 p01 = FP16::cvt2(pv[0], pv[1]), p23 = FP16::cvt2(pv[2], pv[3]);
+    const f16x2 x01 = FP16::cvt2(xv[0], xv[1]), x23 = FP16::cvt2(xv[2], xv[3]);
+    c.pf[par][t2][half + 0] = p01[0];
+    c.pf[par][t2][half + 1] = p01[1];
+    c.pf[par][t2][half + 2] = p23[0];
+    c.pf[par][t2][half + 3] = p23[1];
+    c.xf[par][t2][half + 0] = x01[0];
+    c.xf[par][t2][half + 1] = x01[1];
+    c.xf[par][t2][half + 2] = x23[0];
+    c.xf[par][t2][half + 3] = x23[1];
+  }
+  template <int SL, int K>
+  static __device__ __forceinline__ void pipe_groups_of(State& st, Pipe& c) {
+    if constexpr (group_slot(K, 0) == SL) pipe_group<K, 0>(st, c);
+    if constexpr (group_slot(K, 1) == SL) pipe_group<K, 1>(st, c);
+    if constexpr (group_slot(K, 2) == SL) pipe_group<K, 2>(st, c);
+    if constexpr (group_slot(K, 3) == SL) pipe_group<K, 3>(st, c);
+  }
+  template <int PF, int SL>
+  static __device__ __forceinline__ void pipe_slot(State& st, Pipe& c) {
+    pipe_load<SL + PF>(st, c);
+    constexpr int k = slot_sub(SL), m = slot_m(SL), par = k & 1;
+    if constexpr (SL == blk_start(2)) {
+      pipe_groups_of<SL, 0>(st, c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (slot_kind(SL) == 0) {
+      if constexpr (m == 0) {
+        // S^T starts at -inf for keys past the row (causal) or past kv_limit:
+        // register r holds key j0 + 32 k + 4 hl + 8 (r / 4) + r % 4, visible
+        // iff 32 k + 8 (r / 4) + r % 4 <= lim; 0 elsewhere.
 #pragma unroll
-    for (int t = 0; t < PT; ++t)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const H8 kt = TL::template tr<H8, H4>(kc, st.tb, t * 16, dt);
-        st.acc_a[dt] = FP16::mfma(kt, xf[t], st.acc_a[dt]);
-        st.acc_b[dt] = FP16::mfma(kt, pf[t], st.acc_b[dt]);
+        for (int r = 0; r < 16; ++r)
+          c.s[r] = (k * 32 + (r >> 2) * 8 + (r & 3) <= c.lim) ? 0.f : -INFINITY;
+        c.dp = f32x16{};
       }
+      if constexpr (m & 1) c.dp = E::mfma(c.opv[SL], st.df[m >> 1], c.dp);
+      else c.s = FP16::mfma(c.opd[SL], st.qf[m >> 1], c.s);
+    } else {
+      constexpr int t2 = m / (2 * DT), dt = (m >> 1) % DT;
+      if constexpr (m & 1) st.acc_b[dt] = FP16::mfma(c.opd[SL - 1], c.pf[par][t2], st.acc_b[dt]);
+      else st.acc_a[dt] = FP16::mfma(c.opd[SL], c.xf[par][t2], st.acc_a[dt]);
+    }
+    if constexpr (slot_kind(SL) == 1 && slot_blk(SL) % 2 == 1)
+      pipe_groups_of<SL, (slot_blk(SL) - 1) / 2>(st, c);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int PF, int... SL>
+  static __device__ __forceinline__ void pipe_slots(State& st, Pipe& c,
+                                                    std::integer_sequence<int, SL...>) {
+    (pipe_slot<PF, SL>(st, c), ...);
+  }
+  template <int... SL>
+  static __device__ __forceinline__ void pipe_prologue(State& st, Pipe& c,
+                                                       std::integer_sequence<int, SL...>) {
+    (pipe_load<SL>(st, c), ...);
+  }
+  template <int PF>
+  static __device__ __forceinline__ void pipe_tile(State& st, const char* kc, const char* vc,
+                                                   int j0) {
+    Pipe c;
+    c.kc = kc;
+    c.vc = vc;
+    const int base = j0 + 4 * st.hl;
+    c.lim = st.kv_limit - 1 - base;
+    if (CAUSAL) c.lim = min(c.lim, st.qrow - base);
+    pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
+    pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
 
   // Iteration j: tile j is in (kc, vc); tile j+1 goes into (kn, vn).
   static __device__ __forceinline__ void step(State& st, int j, int n, int n_act, char* kc,
                                               const char* vc, char* kn, char* vn) {
     __builtin_amdgcn_s_waitcnt(0);
-    TL::template to_f16<E>(kc, st.wave, st.lane);
     __syncthreads();
     if (j + 1 < n) issue(st, j + 1, kn, vn);
     if (j >= n_act) return;
-    const int j0 = j * BC;
-    const bool edge = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
-    if (edge) tile<true>(st, kc, vc, j0);
-    else tile<false>(st, kc, vc, j0);
+    pipe_tile<PF>(st, kc, vc, j * BC);
   }
 
   static __device__ void run(const BwdArgs& a, char* k0, char* v0, char* k1, char* v1) {
@@ -279,7 +363,7 @@ struct BwdQ {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.dsum[i] = 0.f;
 
-    st.kp = (const char*)((const T*)a.k + b * a.k_sb + g * a.k_sh);
+    st.kp = (const char*)((const _Float16*)a.k16 + b * a.k_sb + g * a.k_sh);
     st.vp = (const char*)((const T*)a.v + b * a.k_sb + g * a.k_sh);
     st.tile_bytes = (int64_t)BC * a.k_sn * 2;
     st.end_bytes = ((int64_t)(a.Nk - 1) * a.k_sn + a.d) * 2;
@@ -341,8 +425,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(BwdArgs a) {
 // ---------------------------------------------------------- dK / dV kernel
 // One work-group of NW waves per (batch, kv-head, block of NW*32 keys,
 // chunk of q-heads); each wave owns 32 keys, whose K and V fragments (fp16)
-// stay in registers.  Q and dO tiles of BR rows stream through LDS (converted
-// to fp16 there).  Per 32-row sub-block and wave:
+// stay in registers.  Tiles of BR rows of Q and dO (their fp16 copies)
+// stream through LDS.  Per 32-row sub-block and wave:
 //   S  = Q K^T, dP = dO V^T      32x32x16 MFMA, A = Q / dO rows from LDS,
 //                                B = K^T / V^T from registers; each lane holds
 //                                16 query rows of one key
@@ -357,6 +441,7 @@ struct BwdKV {
   static constexpr int QB = BR / 32;
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
+  static constexpr int PF = 3;                // LDS operand read-ahead, in MFMAs
   // per stage: Q tile | dO tile | nl2[BR] | D[BR]
   static constexpr int STAGE_BYTES = 2 * TL::BYTES + 2 * BR * 4;
 
@@ -398,60 +483,150 @@ struct BwdKV {
     TL::load(make_rsrc(st.d0p + o, n), st.off, stage + TL::BYTES, st.wave);
   }
 
-  template <bool EDGE>
-  static __device__ __forceinline__ void tile(State& st, const char* stage, int qt0) {
-    const char* qc = stage;
-    const char* dc = stage + TL::BYTES;
-    const char* sc = stage + 2 * TL::BYTES;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = FP16::mfma(TL::template row<H8>(qc, st.rb, qb * 32, ks), st.kf[ks], s);
-        dp = FP16::mfma(TL::template row<H8>(dc, st.rb, qb * 32, ks), st.vf[ks], dp);
-      }
-      // rows of register r: qt0 + qb*32 + (r/4)*8 + 4 hl + r%4
-      H8 pp[2], dsp[2];
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int lr = qb * 32 + gq * 8 + st.hl * 4;   // local row of e = 0
-        const f32x4 nl = *(const LDS_AS f32x4*)(const LDS_AS void*)(sc + lr * 4);
-        const f32x4 dd = *(const LDS_AS f32x4*)(const LDS_AS void*)(sc + BR * 4 + lr * 4);
-        float pv[4], dsv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = gq * 4 + e;
-          float p = fast_exp2(__builtin_fmaf(s[r], st.c, nl[e]));
-          if constexpr (EDGE) {
-            const int qr = qt0 + lr + e;
-            const bool vis = st.key < st.kv_limit && (!CAUSAL || st.key <= qr);
-            p = vis ? p : 0.f;
-          }
-          pv[e] = p;
-          dsv[e] = p * (dp[r] - dd[e]);
-        }
-        const int t2 = gq >> 1, half = (gq & 1) * 4;
-        const f16x2 p01 = FP16::cvt2(pv[0], pv[1]), p23 = FP16::cvt2(pv[2], pv[3]);
-        const f16x2 s01 = FP16::cvt2(dsv[0], dsv[1]), s23 = FP16::cvt2(dsv[2], dsv[3]);
-        pp[t2][half + 0] = p01[0];
-        pp[t2][half + 1] = p01[1];
-        pp[t2][half + 2] = p23[0];
-        pp[t2][half + 3] = p23[1];
-        dsp[t2][half + 0] = s01[0];
-        dsp[t2][half + 1] = s01[1];
-        dsp[t2][half + 2] = s23[0];
-        dsp[t2][half + 3] = s23[1];
-      }
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int r0 = qb * 32 + t2 * 16;
-          st.dv[dt] = FP16::mfma(pp[t2], TL::template tr<H8, H4>(dc, st.tb, r0, dt), st.dv[dt]);
-          st.dk[dt] = FP16::mfma(dsp[t2], TL::template tr<H8, H4>(qc, st.tb, r0, dt), st.dk[dt]);
-        }
+  // ---- software-pipelined tile ----
+  // Blocks of MFMAs, one S/dP set in flight:
+  //   SD(0) | exp/dS(0) | SD(1) | GR(0)+exp/dS(1) | SD(2) | GR(1)+exp/dS(2) | ...
+  //   | SD(QB-1) | GR(QB-2)+exp/dS(QB-1) | GR(QB-1)
+  // SD(i): the 2 KS S/dP MFMAs of 32-row sub-block i; GR(i): its 4 DT dV/dK
+  // MFMAs (16 each at d = 128).
+  // LDS operands are read PF MFMAs ahead across block boundaries.
+  static constexpr int NBLK = 2 * QB + 1;
+  static constexpr int SDN = 2 * KS;   // MFMAs of an SD block
+  static constexpr int GRN = 4 * DT;   // MFMAs of a GR block
+  static __host__ __device__ constexpr int blk_len(int b) {
+    return (b % 2 == 0) ? (b / 2 < QB ? SDN : GRN) : (b == 1 ? 0 : GRN);
+  }
+  static __host__ __device__ constexpr int blk_start(int b) {
+    int s = 0;
+    for (int q = 0; q < b; ++q) s += blk_len(q);
+    return s;
+  }
+  static constexpr int NSLOT = QB * (SDN + GRN);
+  static __host__ __device__ constexpr int slot_blk(int s) {
+    int b = 0;
+    for (int q = 0; q < NBLK; ++q)
+      if (blk_len(q) > 0 && blk_start(q) <= s) b = q;
+    return b;
+  }
+  // kind 0: S/dP MFMA; kind 1: dV/dK MFMA
+  static __host__ __device__ constexpr int slot_kind(int s) {
+    const int b = slot_blk(s);
+    return (b % 2 == 0 && b / 2 < QB) ? 0 : 1;
+  }
+  static __host__ __device__ constexpr int slot_sub(int s) {
+    const int b = slot_blk(s);
+    return slot_kind(s) == 0 ? b / 2 : (b % 2 == 1 ? (b - 1) / 2 - 1 : QB - 1);
+  }
+  static __host__ __device__ constexpr int slot_m(int s) { return s - blk_start(slot_blk(s)); }
+  // exp/dS group g of sub-block i: after the MFMA of this slot (i >= 1), or
+  // (i = 0) all four before the first MFMA of SD(1)
+  static __host__ __device__ constexpr int group_slot(int i, int g) {
+    return i == 0 ? blk_start(2) : blk_start(2 * i + 1) + g * (GRN / 4);
+  }
+
+  struct Pipe {
+    const char* qc;
+    const char* dc;
+    const char* sc;
+    int dlt;                    // key - qt0 - 4 hl (causal mask)
+    f32x16 s, dp;
+    H8 pp[2][2], dsp[2][2];
+    H8 opd[NSLOT];
+  };
+  template <int SL>
+  static __device__ __forceinline__ void pipe_load(const State& st, Pipe& c) {
+    constexpr int i = slot_sub(SL), m = slot_m(SL);
+    if constexpr (slot_kind(SL) == 0) {
+      c.opd[SL] = TL::template row<H8>((m & 1) ? c.dc : c.qc, st.rb, i * 32, m >> 1);
+    } else {
+      c.opd[SL] = TL::template tr<H8, H4>((m & 1) ? c.qc : c.dc, st.tb, i * 32 + (m / (2 * DT)) * 16,
+                                          (m >> 1) % DT);
     }
+  }
+  template <int I, int GQ>
+  static __device__ __forceinline__ void pipe_group(const State& st, Pipe& c) {
+    constexpr int par = I & 1;
+    const int lr = I * 32 + GQ * 8 + st.hl * 4;
+    const f32x4 nl = *(const LDS_AS f32x4*)(const LDS_AS void*)(c.sc + lr * 4);
+    const f32x4 dd = *(const LDS_AS f32x4*)(const LDS_AS void*)(c.sc + BR * 4 + lr * 4);
+    float pv[4], dsv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, nl[e]));
+      pv[e] = p;
+      dsv[e] = p * (c.dp[GQ * 4 + e] - dd[e]);
+    }
+    constexpr int t2 = GQ >> 1, half = (GQ & 1) * 4;
+    const f16x2 p01 = FP16::cvt2(pv[0], pv[1]), p23 = FP16::cvt2(pv[2], pv[3]);
+    const f16x2 s01 = FP16::cvt2(dsv[0], dsv[1]), s23 = FP16::cvt2(dsv[2], dsv[3]);
+    c.pp[par][t2][half + 0] = p01[0];
+    c.pp[par][t2][half + 1] = p01[1];
+    c.pp[par][t2][half + 2] = p23[0];
+    c.pp[par][t2][half + 3] = p23[1];
+    c.dsp[par][t2][half + 0] = s01[0];
+    c.dsp[par][t2][half + 1] = s01[1];
+    c.dsp[par][t2][half + 2] = s23[0];
+    c.dsp[par][t2][half + 3] = s23[1];
+  }
+  template <int SL, int VI>
+  static __device__ __forceinline__ void pipe_groups_of(const State& st, Pipe& c) {
+    if constexpr (group_slot(VI, 0) == SL) pipe_group<VI, 0>(st, c);
+    if constexpr (group_slot(VI, 1) == SL) pipe_group<VI, 1>(st, c);
+    if constexpr (group_slot(VI, 2) == SL) pipe_group<VI, 2>(st, c);
+    if constexpr (group_slot(VI, 3) == SL) pipe_group<VI, 3>(st, c);
+  }
+  template <int PF, int SL>
+  static __device__ __forceinline__ void pipe_slot(State& st, Pipe& c) {
+    if constexpr (SL + PF < NSLOT) pipe_load<SL + PF>(st, c);
+    constexpr int i = slot_sub(SL), m = slot_m(SL), par = i & 1;
+    if constexpr (SL == blk_start(2)) {
+      pipe_groups_of<SL, 0>(st, c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (slot_kind(SL) == 0) {
+      if constexpr (m == 0) {
+        // Causal: S starts at -inf where the key lies after the row
+        // (key <= row  <=>  key - qt0 - 4 hl <= 32 i + 8 (r / 4) + r % 4 for
+        // register r), so that P = 0 and dS = 0 there; 0 elsewhere.
+        if constexpr (CAUSAL) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            c.s[r] = (c.dlt <= i * 32 + (r >> 2) * 8 + (r & 3)) ? 0.f : -INFINITY;
+        } else {
+          c.s = f32x16{};
+        }
+        c.dp = f32x16{};
+      }
+      if constexpr (m & 1) c.dp = FP16::mfma(c.opd[SL], st.vf[m >> 1], c.dp);
+      else c.s = FP16::mfma(c.opd[SL], st.kf[m >> 1], c.s);
+    } else {
+      constexpr int t2 = m / (2 * DT), dt = (m >> 1) % DT;
+      if constexpr (m & 1) st.dk[dt] = FP16::mfma(c.dsp[par][t2], c.opd[SL], st.dk[dt]);
+      else st.dv[dt] = FP16::mfma(c.pp[par][t2], c.opd[SL], st.dv[dt]);
+    }
+    if constexpr (slot_kind(SL) == 1 && slot_blk(SL) % 2 == 1)
+      pipe_groups_of<SL, (slot_blk(SL) - 1) / 2>(st, c);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int PF, int... SL>
+  static __device__ __forceinline__ void pipe_slots(State& st, Pipe& c,
+                                                    std::integer_sequence<int, SL...>) {
+    (pipe_slot<PF, SL>(st, c), ...);
+  }
+  template <int... SL>
+  static __device__ __forceinline__ void pipe_prologue(State& st, Pipe& c,
+                                                       std::integer_sequence<int, SL...>) {
+    (pipe_load<SL>(st, c), ...);
+  }
+  template <int PF>
+  static __device__ __forceinline__ void pipe_tile(State& st, const char* stage, int qt0) {
+    Pipe c;
+    c.qc = stage;
+    c.dc = stage + TL::BYTES;
+    c.sc = stage + 2 * TL::BYTES;
+    c.dlt = st.key - qt0 - 4 * st.hl;
+    pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
+    pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
 
   // Iteration t over (head, q-tile) pairs: tile t (rows qt0..) is in `cur`,
@@ -459,15 +634,13 @@ struct BwdKV {
   static __device__ __forceinline__ void step(const BwdArgs& a, State& st, int t, int n_t, int qt0,
                                               int hn, int qn, char* cur, char* nxt, bool live) {
     __builtin_amdgcn_s_waitcnt(0);
-    TL::template to_f16<E>(cur, st.wave, st.lane);
-    TL::template to_f16<E>(cur + TL::BYTES, st.wave, st.lane);
     __syncthreads();
     if (t + 1 < n_t) issue(a, st, hn, qn, nxt);
     if (!live) return;                                   // this wave's keys are all masked
     if (CAUSAL && qt0 + BR - 1 < st.kw0) return;         // no row of the tile sees them
-    const bool edge = (CAUSAL && qt0 < st.kw0 + 31) || (st.kw0 + 32 > st.kv_limit);
-    if (edge) tile<true>(st, cur, qt0);
-    else tile<false>(st, cur, qt0);
+    // Keys at or past kv_limit are not masked here: a key's P and dS only
+    // reach its own rows of dK / dV, which are stored as zero.
+    pipe_tile<PF>(st, cur, qt0);
   }
 
   static __device__ void run(const BwdArgs& a, char* s0, char* s1) {
@@ -511,8 +684,8 @@ struct BwdKV {
       st.dv[dt] = f32x16{};
     }
     st.c = a.c;
-    st.q0p = (const char*)((const T*)a.q + b * a.q_sb);
-    st.d0p = (const char*)((const T*)a.dout + b * a.q_sb);
+    st.q0p = (const char*)((const _Float16*)a.q16 + b * a.q_sb);
+    st.d0p = (const char*)((const _Float16*)a.do16 + b * a.q_sb);
     st.head_bytes = a.q_sh * 2;
     st.row_bytes = a.q_sn * 2;
     st.end_bytes = ((int64_t)(a.Nq - 1) * a.q_sn + a.d) * 2;
@@ -566,7 +739,9 @@ struct BwdKV {
         const int kr = st.kw0 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
         if (kr >= a.Nk) continue;
         const int64_t off = b * a.k_sb + g * a.k_sh + kr * a.k_sn + col;
-        const float kval = st.dk[dt][r] * a.scale, vval = st.dv[dt][r];
+        const bool kv_ok = kr < st.kv_limit;
+        const float kval = kv_ok ? st.dk[dt][r] * a.scale : 0.f;
+        const float vval = kv_ok ? st.dv[dt][r] : 0.f;
         if (!direct) {
           a.part_dk[chunk * part + off] = kval;
           a.part_dv[chunk * part + off] = vval;

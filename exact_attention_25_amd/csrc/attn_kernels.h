@@ -36,6 +36,11 @@ struct BwdArgs {
   const void* o;
   const float* lse;
   const void* dout;
+  // fp16 copies of q, dout and k (same strides) for the products that take
+  // P or dS; for fp16 inputs they are q, dout and k themselves
+  const void* q16;
+  const void* do16;
+  const void* k16;
   void* dq;
   void* dk;
   void* dv;

@@ -110,9 +110,9 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
 /* Bytes of device workspace attn_bwd needs for *p (0 if p is invalid): two
- * [B, Hq, Nq rounded up to 64] float arrays (D and -LSE*log2(e)) plus, when
- * the q-heads of a kv-head are split over several work-groups, fp32 partial
- * dK and dV sums. */
+ * [B, Hq, Nq rounded up to 128] float arrays (D and -LSE*log2(e)); when the
+ * q-heads of a kv-head are split over several work-groups, fp32 partial dK
+ * and dV sums; for bf16 inputs, fp16 copies of q, dout and k. */
 size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /* Backward pass: gradients of <dout, O> with O = attention(q, k, v), with the
