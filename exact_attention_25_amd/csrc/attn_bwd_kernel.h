@@ -26,22 +26,24 @@
 // row and for the padding rows past Nq, so that P = 0 there).
 //
 // Tiles of 128 rows (dK/dV) or keys (dQ) stream through LDS, double-
-// buffered, with a padded row pitch of D/8 + 1 16-byte slots, filled by
-// direct buffer->LDS loads (rows or columns past the tensor read as zero).
-// Row-fragment reads (16 rows x one 16-byte chunk per 16 lanes) are
-// conflict-free; transposed reads (4 rows x 64 bytes per half-wave) share
-// banks pairwise.  Every read address is a per-lane base plus a compile-time
-// offset.
+// buffered, filled by direct buffer->LDS loads (rows or columns past the
+// tensor read as zero).  At D = 128 the 16-byte chunks of a row are XOR-
+// swizzled (SwzTile), which keeps both the row-fragment reads and the
+// transposed reads free of bank conflicts; at D = 64 rows are padded to
+// D/8 + 1 slots (PadTile: row reads conflict-free, transposed reads sharing
+// banks pairwise).  Every read address is a per-lane base plus a
+// compile-time offset.
 //
 // Both kernels run a tile as a fixed software pipeline over its four 32-row
 // (32-key) sub-blocks, one wave per SIMD: the S/dP products of sub-block i
 // are issued while the dV/dK (A/B) products of sub-block i-1 run beside the
 // exponentials of sub-block i, and each LDS operand is read PF products
-// ahead.  Masking costs no per-element work in the loop: the S accumulator
-// of a sub-block starts at -inf where a key is excluded (causal, and in the
-// dQ kernel also keys past kv_lens), 0 elsewhere, so P = 0 and dS = 0 there.
-// The dK/dV kernel leaves keys past kv_lens unmasked: their P and dS reach
-// only their own rows of dK and dV, which it stores as zero.
+// ahead.  Masking costs no per-element work in the loop: on a tile with
+// excluded keys (causal, and in the dQ kernel also keys past kv_lens) the S
+// accumulator of a sub-block starts at -inf where a key is excluded and 0
+// elsewhere, so P = 0 and dS = 0 there; other tiles start from the MFMA's
+// zero operand.  The dK/dV kernel leaves keys past kv_lens unmasked: their
+// P and dS reach only their own rows of dK and dV, which it stores as zero.
 #pragma once
 
 #include <type_traits>
@@ -94,26 +96,93 @@ struct PadTile {
   // Lane bases: row fragment (row l32, chunk hl) and transposed read (row
   // 4 (group / 2) + i / 4, column 16 (group % 2) + 4 (i % 4) for lane i of
   // 16-lane group `group`).
-  static __device__ __forceinline__ int row_base(int l32, int hl) { return l32 * P + hl * 16; }
-  static __device__ __forceinline__ int tr_base(int lane) {
-    const int grp = lane >> 4, gi = lane & 15;
-    return (4 * (grp >> 1) + (gi >> 2)) * P + (16 * (grp & 1) + 4 * (gi & 3)) * 2;
+  struct Bases {
+    int rb, tb;
+  };
+  static __device__ __forceinline__ Bases bases(int lane) {
+    const int l32 = lane & 31, hl = lane >> 5, grp = lane >> 4, gi = lane & 15;
+    return {l32 * P + hl * 16,
+            (4 * (grp >> 1) + (gi >> 2)) * P + (16 * (grp & 1) + 4 * (gi & 3)) * 2};
   }
   // MFMA operand from rows r0 + (lane % 32), k-step ks (d = 16 ks + 8 hl ..).
   template <class V8>
-  static __device__ __forceinline__ V8 row(const char* buf, int rb, int r0, int ks) {
-    return lds_read16<V8>(buf + rb + r0 * P + ks * 32);
+  static __device__ __forceinline__ V8 row(const char* buf, const Bases& b, int r0, int ks) {
+    return lds_read16<V8>(buf + b.rb + r0 * P + ks * 32);
   }
   // MFMA operand read transposed: column dt*32 + lane%32, rows r0 + slot
   // order 8 (s / 4) + 4 hl + s % 4 for slot s.
   template <class V8, class V4>
-  static __device__ __forceinline__ V8 tr(const char* buf, int tb, int r0, int dt) {
-    const char* p = buf + tb + r0 * P + dt * 64;
+  static __device__ __forceinline__ V8 tr(const char* buf, const Bases& b, int r0, int dt) {
+    const char* p = buf + b.tb + r0 * P + dt * 64;
     const V4 lo = lds_read_tr4<V4>(p);
     const V4 hi = lds_read_tr4<V4>(p + 8 * P);
     return concat4<V8, V4>(lo, hi);
   }
 };
+
+// The same tile for D = 128 without padding: rows of 16 chunks of 16 bytes,
+// chunk c of row r stored at position c ^ f(r), f(r) = 4 (r % 4) + (r / 4) % 4.
+// The 16 rows of a row-fragment read land on 16 distinct chunk positions, and
+// so do the 4 rows x 4 chunks of a transposed read by 32 lanes: both are
+// free of bank conflicts.  The XOR is folded into per-lane bases (one per
+// k-step, and per 32-column block and half of a transposed read), since
+// r0 is a multiple of 16 in every read.
+template <int R, int NW>
+struct SwzTile {
+  static constexpr int D = 128;
+  static constexpr int CPR = 16;
+  static constexpr int P = 256;                     // pitch in bytes
+  static constexpr int BYTES = R * P;
+  static constexpr int INS = R * CPR / 64;          // load instructions per tile
+  static constexpr int IPW = (INS + NW - 1) / NW;
+  static __host__ __device__ constexpr int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+  static __device__ __forceinline__ uint32_t offset(int ins, int lane, int dchunks, int64_t sn) {
+    const int s = ins * 64 + lane;
+    const int r = s >> 4, lc = (s & 15) ^ f(r & 15);
+    if (r >= R || lc >= dchunks) return kBufOutOfRange;
+    return (uint32_t)((r * sn + lc * 8) * 2);
+  }
+  static __device__ __forceinline__ void load(BufRsrc rs, const uint32_t (&off)[IPW], char* buf,
+                                              int wave) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int ins = i * NW + wave;
+      if (ins < INS) dma16_buf(rs, off[i], buf + ins * 1024);
+    }
+  }
+  struct Bases {
+    int rb[8];        // row fragment, k-step ks
+    int tb[4][2];     // transposed read, 32-column block dt, rows +0 / +8
+  };
+  static __device__ __forceinline__ Bases bases(int lane) {
+    const int l32 = lane & 31, hl = lane >> 5, grp = lane >> 4, gi = lane & 15;
+    Bases b;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) b.rb[ks] = l32 * P + (((2 * ks + hl) ^ f(l32 & 15)) << 4);
+    const int rr = 4 * (grp >> 1) + (gi >> 2);           // row within 16
+    const int lc = 2 * (grp & 1) + ((gi & 3) >> 1);      // chunk within a 64-byte block
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        b.tb[dt][h] = (rr + 8 * h) * P + (((dt * 4 + lc) ^ f(rr + 8 * h)) << 4) + (gi & 1) * 8;
+    return b;
+  }
+  template <class V8>
+  static __device__ __forceinline__ V8 row(const char* buf, const Bases& b, int r0, int ks) {
+    return lds_read16<V8>(buf + b.rb[ks] + r0 * P);
+  }
+  template <class V8, class V4>
+  static __device__ __forceinline__ V8 tr(const char* buf, const Bases& b, int r0, int dt) {
+    const V4 lo = lds_read_tr4<V4>(buf + b.tb[dt][0] + r0 * P);
+    const V4 hi = lds_read_tr4<V4>(buf + b.tb[dt][1] + r0 * P);
+    return concat4<V8, V4>(lo, hi);
+  }
+};
+
+template <int R, int D, int NW>
+using BwdTile = typename std::conditional<D == 128, SwzTile<R, NW>, PadTile<R, D, NW>>::type;
 
 // --------------------------------------------------------------- dQ kernel
 // One work-group of NW waves per (batch, q-head, block of NW*32 rows); each
@@ -128,7 +197,7 @@ struct PadTile {
 // Epilogue: dQ = scale (A - D B); D and nl2 to the workspace.
 template <class E, int D, int NW, int BC, bool CAUSAL>
 struct BwdQ {
-  using TL = PadTile<BC, D, NW>;
+  using TL = BwdTile<BC, D, NW>;
   static constexpr int ROWS = NW * 32;
   static constexpr int KB = BC / 32;
   static constexpr int KS = D / 16;
@@ -143,7 +212,7 @@ struct BwdQ {
   struct State {
     int lane, wave, hl, l32;
     int q_w0, qrow, kv_limit;
-    int rb, tb;                 // LDS lane bases
+    typename TL::Bases lb;      // LDS lane bases
     const char* kp;             // K / V of this (batch, kv-head), key 0
     const char* vp;
     int64_t tile_bytes, end_bytes;
@@ -207,6 +276,7 @@ struct BwdQ {
     const char* kc;
     const char* vc;
     int lim;                    // keys with offset > lim are masked (see pipe_slot)
+    bool msk;                   // the tile has masked keys for this wave
     f32x16 s, dp;
     H8 pf[2][2], xf[2][2];
     H8 opd[NSLOT];
@@ -217,10 +287,10 @@ struct BwdQ {
     if constexpr (SL < NSLOT && slot_reads(SL)) {
       constexpr int k = slot_sub(SL), m = slot_m(SL);
       if constexpr (slot_kind(SL) == 0) {
-        if constexpr (m & 1) c.opv[SL] = TL::template row<V8>(c.vc, st.rb, k * 32, m >> 1);
-        else c.opd[SL] = TL::template row<H8>(c.kc, st.rb, k * 32, m >> 1);
+        if constexpr (m & 1) c.opv[SL] = TL::template row<V8>(c.vc, st.lb, k * 32, m >> 1);
+        else c.opd[SL] = TL::template row<H8>(c.kc, st.lb, k * 32, m >> 1);
       } else {
-        c.opd[SL] = TL::template tr<H8, H4>(c.kc, st.tb, k * 32 + (m / (2 * DT)) * 16, (m >> 1) % DT);
+        c.opd[SL] = TL::template tr<H8, H4>(c.kc, st.lb, k * 32 + (m / (2 * DT)) * 16, (m >> 1) % DT);
       }
     }
   }
@@ -264,16 +334,27 @@ struct BwdQ {
     }
     if constexpr (slot_kind(SL) == 0) {
       if constexpr (m == 0) {
-        // S^T starts at -inf for keys past the row (causal) or past kv_limit:
-        // register r holds key j0 + 32 k + 4 hl + 8 (r / 4) + r % 4, visible
-        // iff 32 k + 8 (r / 4) + r % 4 <= lim; 0 elsewhere.
+        // On a tile with masked keys, S^T starts at -inf for keys past the
+        // row (causal) or past kv_limit: register r holds key
+        // j0 + 32 k + 4 hl + 8 (r / 4) + r % 4, visible iff
+        // 32 k + 8 (r / 4) + r % 4 <= lim; 0 elsewhere.  Other tiles start
+        // from the MFMA's zero operand.
+        if (c.msk) {
+          f32x16 init;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          c.s[r] = (k * 32 + (r >> 2) * 8 + (r & 3) <= c.lim) ? 0.f : -INFINITY;
-        c.dp = f32x16{};
+          for (int r = 0; r < 16; ++r)
+            init[r] = (k * 32 + (r >> 2) * 8 + (r & 3) <= c.lim) ? 0.f : -INFINITY;
+          c.s = FP16::mfma(c.opd[SL], st.qf[0], init);
+        } else {
+          c.s = FP16::mfma(c.opd[SL], st.qf[0], f32x16{});
+        }
+      } else if constexpr (m == 1) {
+        c.dp = E::mfma(c.opv[SL], st.df[0], f32x16{});
+      } else if constexpr (m & 1) {
+        c.dp = E::mfma(c.opv[SL], st.df[m >> 1], c.dp);
+      } else {
+        c.s = FP16::mfma(c.opd[SL], st.qf[m >> 1], c.s);
       }
-      if constexpr (m & 1) c.dp = E::mfma(c.opv[SL], st.df[m >> 1], c.dp);
-      else c.s = FP16::mfma(c.opd[SL], st.qf[m >> 1], c.s);
     } else {
       constexpr int t2 = m / (2 * DT), dt = (m >> 1) % DT;
       if constexpr (m & 1) st.acc_b[dt] = FP16::mfma(c.opd[SL - 1], c.pf[par][t2], st.acc_b[dt]);
@@ -302,6 +383,7 @@ struct BwdQ {
     const int base = j0 + 4 * st.hl;
     c.lim = st.kv_limit - 1 - base;
     if (CAUSAL) c.lim = min(c.lim, st.qrow - base);
+    c.msk = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
     pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
     pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
@@ -371,8 +453,7 @@ struct BwdQ {
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i)
       st.off[i] = TL::offset(i * NW + st.wave, st.lane, dchunks, a.k_sn);
-    st.rb = TL::row_base(st.l32, st.hl);
-    st.tb = TL::tr_base(st.lane);
+    st.lb = TL::bases(st.lane);
 
     if (n_tiles > 0) issue(st, 0, k0, v0);
     for (int j = 0; j < n_tiles; j += 2) {
@@ -436,7 +517,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(BwdArgs a) {
 //                                read transposed from LDS
 template <class E, int D, int NW, int BR, bool CAUSAL>
 struct BwdKV {
-  using TL = PadTile<BR, D, NW>;
+  using TL = BwdTile<BR, D, NW>;
   static constexpr int KEYS = NW * 32;
   static constexpr int QB = BR / 32;
   static constexpr int KS = D / 16;
@@ -453,7 +534,7 @@ struct BwdKV {
   struct State {
     int lane, wave, hl, l32;
     int b, kw0, key, kv_limit;
-    int rb, tb;
+    typename TL::Bases lb;      // LDS lane bases
     int64_t head_bytes;         // bytes between the Q (dO) rows of consecutive heads
     int64_t row_bytes;          // bytes per Q row
     int64_t end_bytes;          // bytes from a head's row 0 to the end of row Nq-1
@@ -529,6 +610,7 @@ struct BwdKV {
     const char* dc;
     const char* sc;
     int dlt;                    // key - qt0 - 4 hl (causal mask)
+    bool msk;                   // causal: the tile crosses this wave's diagonal
     f32x16 s, dp;
     H8 pp[2][2], dsp[2][2];
     H8 opd[NSLOT];
@@ -537,9 +619,9 @@ struct BwdKV {
   static __device__ __forceinline__ void pipe_load(const State& st, Pipe& c) {
     constexpr int i = slot_sub(SL), m = slot_m(SL);
     if constexpr (slot_kind(SL) == 0) {
-      c.opd[SL] = TL::template row<H8>((m & 1) ? c.dc : c.qc, st.rb, i * 32, m >> 1);
+      c.opd[SL] = TL::template row<H8>((m & 1) ? c.dc : c.qc, st.lb, i * 32, m >> 1);
     } else {
-      c.opd[SL] = TL::template tr<H8, H4>((m & 1) ? c.qc : c.dc, st.tb, i * 32 + (m / (2 * DT)) * 16,
+      c.opd[SL] = TL::template tr<H8, H4>((m & 1) ? c.qc : c.dc, st.lb, i * 32 + (m / (2 * DT)) * 16,
                                           (m >> 1) % DT);
     }
   }
@@ -585,20 +667,27 @@ struct BwdKV {
     }
     if constexpr (slot_kind(SL) == 0) {
       if constexpr (m == 0) {
-        // Causal: S starts at -inf where the key lies after the row
-        // (key <= row  <=>  key - qt0 - 4 hl <= 32 i + 8 (r / 4) + r % 4 for
-        // register r), so that P = 0 and dS = 0 there; 0 elsewhere.
-        if constexpr (CAUSAL) {
+        // Causal, on a tile that crosses the diagonal: S starts at -inf
+        // where the key lies after the row (key <= row  <=>
+        // key - qt0 - 4 hl <= 32 i + 8 (r / 4) + r % 4 for register r), so
+        // that P = 0 and dS = 0 there; 0 elsewhere.  Other tiles start from
+        // the MFMA's zero operand.
+        if (CAUSAL && c.msk) {
+          f32x16 init;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            c.s[r] = (c.dlt <= i * 32 + (r >> 2) * 8 + (r & 3)) ? 0.f : -INFINITY;
+            init[r] = (c.dlt <= i * 32 + (r >> 2) * 8 + (r & 3)) ? 0.f : -INFINITY;
+          c.s = FP16::mfma(c.opd[SL], st.kf[0], init);
         } else {
-          c.s = f32x16{};
+          c.s = FP16::mfma(c.opd[SL], st.kf[0], f32x16{});
         }
-        c.dp = f32x16{};
+      } else if constexpr (m == 1) {
+        c.dp = FP16::mfma(c.opd[SL], st.vf[0], f32x16{});
+      } else if constexpr (m & 1) {
+        c.dp = FP16::mfma(c.opd[SL], st.vf[m >> 1], c.dp);
+      } else {
+        c.s = FP16::mfma(c.opd[SL], st.kf[m >> 1], c.s);
       }
-      if constexpr (m & 1) c.dp = FP16::mfma(c.opd[SL], st.vf[m >> 1], c.dp);
-      else c.s = FP16::mfma(c.opd[SL], st.kf[m >> 1], c.s);
     } else {
       constexpr int t2 = m / (2 * DT), dt = (m >> 1) % DT;
       if constexpr (m & 1) st.dk[dt] = FP16::mfma(c.dsp[par][t2], c.opd[SL], st.dk[dt]);
@@ -625,6 +714,7 @@ struct BwdKV {
     c.dc = stage + TL::BYTES;
     c.sc = stage + 2 * TL::BYTES;
     c.dlt = st.key - qt0 - 4 * st.hl;
+    c.msk = qt0 < st.kw0 + 31;
     pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
     pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
@@ -693,8 +783,7 @@ struct BwdKV {
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i)
       st.off[i] = TL::offset(i * NW + st.wave, st.lane, dchunks, a.q_sn);
-    st.rb = TL::row_base(st.l32, st.hl);
-    st.tb = TL::tr_base(st.lane);
+    st.lb = TL::bases(st.lane);
 
     // query rows that can see some key of this block
     const int q_start = CAUSAL ? (key0 / BR) * BR : 0;
