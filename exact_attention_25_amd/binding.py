@@ -143,15 +143,7 @@ def attn_fwd(q, k, v, *, layout="bhnd", causal=False, scale=None, attn_mask=None
     torch = _torch()
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
-    mask_ptr, mstr = None, (0, 0, 0)
-    if attn_mask is not None:
-        if attn_mask.dtype != torch.float32 or not attn_mask.is_cuda:
-            raise ValueError("attn_mask must be a float32 device tensor")
-        m = attn_mask.expand(B, Hq, Nq, Nk)
-        if m.stride(3) != 1:
-            m = m.contiguous()
-        attn_mask = m
-        mask_ptr, mstr = m.data_ptr(), (m.stride(0), m.stride(1), m.stride(2))
+    attn_mask, mask_ptr, mstr = _mask_arg(attn_mask, B, Hq, Nq, Nk)
     lens_ptr = None
     if kv_lens is not None:
         if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
@@ -171,14 +163,32 @@ def attn_fwd(q, k, v, *, layout="bhnd", causal=False, scale=None, attn_mask=None
     return out, lse
 
 
-def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, kv_lens=None,
-             grad_dtype="fp32", workspace=None):
-    """Backward attention from the forward's (o, lse).  Returns (dq, dk, dv)."""
+def _mask_arg(attn_mask, B, Hq, Nq, Nk):
+    """(tensor, pointer, strides) for an additive float32 mask broadcastable to
+    [B,Hq,Nq,Nk], or (None, None, (0, 0, 0))."""
+    torch = _torch()
+    if attn_mask is None:
+        return None, None, (0, 0, 0)
+    if attn_mask.dtype != torch.float32 or not attn_mask.is_cuda:
+        raise ValueError("attn_mask must be a float32 device tensor")
+    m = attn_mask.expand(B, Hq, Nq, Nk)
+    if m.stride(3) != 1:
+        m = m.contiguous()
+    return m, m.data_ptr(), (m.stride(0), m.stride(1), m.stride(2))
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, attn_mask=None,
+             kv_lens=None, grad_dtype="fp32", workspace=None):
+    """Backward attention from the forward's (o, lse).  Returns (dq, dk, dv).
+
+    attn_mask: the same optional additive float32 mask the forward took.
+    """
     torch = _torch()
     lib = load()
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
     if dout.shape != q.shape or o.shape != q.shape:
         raise ValueError("o and dout must have q's shape")
+    attn_mask, mask_ptr, mstr = _mask_arg(attn_mask, B, Hq, Nq, Nk)
     lens_ptr = None
     if kv_lens is not None:
         if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
@@ -186,7 +196,7 @@ def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, 
         kv_lens = kv_lens.contiguous()
         lens_ptr = kv_lens.data_ptr()
     p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
-                    causal, None, (0, 0, 0), lens_ptr)
+                    causal, mask_ptr, mstr, lens_ptr)
     gcode = ATTN_FP32 if grad_dtype == "fp32" else _dtype_code(q.dtype)
     gdt = torch.float32 if gcode == ATTN_FP32 else q.dtype
     dq = torch.empty(q.shape, dtype=gdt, device=q.device)

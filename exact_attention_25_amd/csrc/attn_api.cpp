@@ -39,10 +39,7 @@ attn_status attn_validate(const attn_params* p, int for_backward) {
   if (p->causal && p->Nq != p->Nk) return ATTN_EINVAL;
   if (p->mask && (p->mask_sb < 0 || p->mask_sh < 0 || p->mask_sq < 0)) return ATTN_EINVAL;
   if (p->d < 8 || p->d > 128 || p->d % 8 != 0) return ATTN_EUNSUPPORTED;
-  if (for_backward) {
-    if (p->mask) return ATTN_EUNSUPPORTED;
-    if (p->dtype == ATTN_FP32) return ATTN_EUNSUPPORTED;
-  }
+  if (for_backward && p->dtype == ATTN_FP32) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -137,6 +134,7 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return ATTN_EALIGN;
   if (p->kv_lens && (reinterpret_cast<uintptr_t>(p->kv_lens) & 3u)) return ATTN_EALIGN;
+  if (p->mask && (reinterpret_cast<uintptr_t>(p->mask) & 3u)) return ATTN_EALIGN;
   if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_EWORKSPACE;
 
   attn::BwdArgs a = {};
@@ -161,6 +159,8 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.kv_chunks = ws.chunks;
   a.ld_rows = ws.ld;
   a.kv_lens = p->kv_lens;
+  a.mask = p->mask;
+  a.m_sb = p->mask_sb; a.m_sh = p->mask_sh; a.m_sq = p->mask_sq;
   const Strides sq = strides_for(p->layout, p->Hq, p->Nq, p->d);
   const Strides sk = strides_for(p->layout, p->Hkv, p->Nk, p->d);
   a.q_sb = sq.sb; a.q_sh = sq.sh; a.q_sn = sq.sn;

@@ -54,15 +54,25 @@ static hipError_t launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
   if (a.Nq > 0) {
     const int nqb = (a.Nq + NW_Q * 32 - 1) / (NW_Q * 32);
     dim3 grid((unsigned)(a.B * a.Hq * nqb)), block(NW_Q * 64);
-    if (causal) hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, false>), grid, block, 0, st, a);
+    if (a.mask) {
+      if (causal) hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, true, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, false, true>), grid, block, 0, st, a);
+    } else {
+      if (causal) hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, true, false>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, false, false>), grid, block, 0, st, a);
+    }
   }
   // dK / dV (after dQ: it reads D and nl2)
   if (a.Nk > 0) {
     const int nkb = (a.Nk + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock;
     dim3 grid((unsigned)(a.B * a.Hkv * a.kv_chunks * nkb)), block(NW_KV * 64);
-    if (causal) hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, false>), grid, block, 0, st, a);
+    if (a.mask) {
+      if (causal) hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, true, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, false, true>), grid, block, 0, st, a);
+    } else {
+      if (causal) hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, true, false>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, false, false>), grid, block, 0, st, a);
+    }
     if (a.kv_chunks > 1) {
       const int64_t n = (int64_t)a.B * a.Hkv * a.Nk * a.d;
       const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);

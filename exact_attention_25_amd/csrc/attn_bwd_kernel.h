@@ -195,7 +195,7 @@ using BwdTile = typename std::conditional<D == 128, SwzTile<R, NW>, PadTile<R, D
 //   A^T += K^T X^T, B^T += K^T P^T    32x32x16 fp16 MFMA, K^T read transposed
 //                                     from LDS, X^T / P^T from registers
 // Epilogue: dQ = scale (A - D B); D and nl2 to the workspace.
-template <class E, int D, int NW, int BC, bool CAUSAL>
+template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
 struct BwdQ {
   using TL = BwdTile<BC, D, NW>;
   static constexpr int ROWS = NW * 32;
@@ -218,6 +218,8 @@ struct BwdQ {
     int64_t tile_bytes, end_bytes;
     uint32_t off[TL::IPW];
     float c, nl2;
+    const float* mrow;          // additive mask row of this lane's query (MASK)
+    int nk1;                    // Nk - 1
     H8 qf[KS];
     V8 df[KS];
     f32x16 acc_a[DT], acc_b[DT];
@@ -277,6 +279,8 @@ struct BwdQ {
     const char* vc;
     int lim;                    // keys with offset > lim are masked (see pipe_slot)
     bool msk;                   // the tile has masked keys for this wave
+    int j0;                     // first key of the tile
+    float mv[KB][16];           // additive mask values per key block (MASK)
     f32x16 s, dp;
     H8 pf[2][2], xf[2][2];
     H8 opd[NSLOT];
@@ -294,13 +298,24 @@ struct BwdQ {
       }
     }
   }
+  // Additive mask values of key block K for this lane's row: register r
+  // holds key j0 + 32 K + 8 (r / 4) + 4 hl + r % 4 (clamped to the last key;
+  // keys past Nk are excluded through S anyway).
+  template <int K>
+  static __device__ __forceinline__ void pipe_mask(const State& st, Pipe& c) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      c.mv[K][r] = st.mrow[min(c.j0 + K * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3), st.nk1)];
+  }
   template <int K, int GQ>
   static __device__ __forceinline__ void pipe_group(State& st, Pipe& c) {
     constexpr int par = K & 1;
     float pv[4], xv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, st.nl2));
+      // P = exp2(s c + mask log2(e) - LSE log2(e))
+      const float ml = MASK ? __builtin_fmaf(c.mv[K][GQ * 4 + e], kLog2e, st.nl2) : st.nl2;
+      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, ml));
       pv[e] = p;
       xv[e] = p * c.dp[GQ * 4 + e];
       st.dsum[e] += xv[e];
@@ -332,6 +347,7 @@ struct BwdQ {
       pipe_groups_of<SL, 0>(st, c);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (MASK && slot_kind(SL) == 0 && m == 0) pipe_mask<k>(st, c);
     if constexpr (slot_kind(SL) == 0) {
       if constexpr (m == 0) {
         // On a tile with masked keys, S^T starts at -inf for keys past the
@@ -384,6 +400,7 @@ struct BwdQ {
     c.lim = st.kv_limit - 1 - base;
     if (CAUSAL) c.lim = min(c.lim, st.qrow - base);
     c.msk = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
+    c.j0 = j0;
     pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
     pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
@@ -436,6 +453,8 @@ struct BwdQ {
     }
     const float lse = a.lse[((int64_t)b * a.Hq + h) * a.Nq + crow];
     st.nl2 = (st.qrow < a.Nq && lse != -INFINITY) ? -lse * kLog2e : -INFINITY;
+    st.nk1 = a.Nk - 1;
+    if (MASK) st.mrow = a.mask + b * a.m_sb + h * a.m_sh + (int64_t)crow * a.m_sq;
     st.c = a.c;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -493,9 +512,9 @@ struct BwdQ {
   }
 };
 
-template <class E, int D, int NW, int BC, bool CAUSAL>
+template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(BwdArgs a) {
-  using K = BwdQ<E, D, NW, BC, CAUSAL>;
+  using K = BwdQ<E, D, NW, BC, CAUSAL, MASK>;
   __shared__ __attribute__((aligned(1024))) char k0[K::TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::TL::BYTES];
@@ -515,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(BwdArgs a) {
 //   dV += P^T dO, dK += dS^T Q   32x32x16 MFMA, A = P^T / dS^T from the same
 //                                registers (query slots matched), B = dO / Q
 //                                read transposed from LDS
-template <class E, int D, int NW, int BR, bool CAUSAL>
+template <class E, int D, int NW, int BR, bool CAUSAL, bool MASK>
 struct BwdKV {
   using TL = BwdTile<BR, D, NW>;
   static constexpr int KEYS = NW * 32;
@@ -542,6 +561,7 @@ struct BwdKV {
     const char* d0p;
     uint32_t off[TL::IPW];
     float c;
+    int nq1;                    // Nq - 1
     H8 kf[KS], vf[KS];
     f32x16 dk[DT], dv[DT];
   };
@@ -611,6 +631,10 @@ struct BwdKV {
     const char* sc;
     int dlt;                    // key - qt0 - 4 hl (causal mask)
     bool msk;                   // causal: the tile crosses this wave's diagonal
+    int qt0;                    // first row of the tile
+    const float* mcol;          // additive mask column of this lane's key, tile's head (MASK)
+    int64_t msq;                // mask row stride
+    float mv[QB][16];           // additive mask values per sub-block (MASK)
     f32x16 s, dp;
     H8 pp[2][2], dsp[2][2];
     H8 opd[NSLOT];
@@ -625,6 +649,15 @@ struct BwdKV {
                                           (m >> 1) % DT);
     }
   }
+  // Additive mask values of sub-block I for this lane's key: register r holds
+  // row qt0 + 32 I + 8 (r / 4) + 4 hl + r % 4 (clamped to the last row; rows
+  // past Nq have P = 0 through nl2).
+  template <int I>
+  static __device__ __forceinline__ void pipe_mask(const State& st, Pipe& c) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      c.mv[I][r] = c.mcol[min(c.qt0 + I * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3), st.nq1) * c.msq];
+  }
   template <int I, int GQ>
   static __device__ __forceinline__ void pipe_group(const State& st, Pipe& c) {
     constexpr int par = I & 1;
@@ -634,7 +667,9 @@ struct BwdKV {
     float pv[4], dsv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, nl[e]));
+      // P = exp2(s c + mask log2(e) - LSE log2(e))
+      const float ml = MASK ? __builtin_fmaf(c.mv[I][GQ * 4 + e], kLog2e, nl[e]) : nl[e];
+      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, ml));
       pv[e] = p;
       dsv[e] = p * (c.dp[GQ * 4 + e] - dd[e]);
     }
@@ -665,6 +700,7 @@ struct BwdKV {
       pipe_groups_of<SL, 0>(st, c);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (MASK && slot_kind(SL) == 0 && m == 0) pipe_mask<i>(st, c);
     if constexpr (slot_kind(SL) == 0) {
       if constexpr (m == 0) {
         // Causal, on a tile that crosses the diagonal: S starts at -inf
@@ -708,21 +744,28 @@ struct BwdKV {
     (pipe_load<SL>(st, c), ...);
   }
   template <int PF>
-  static __device__ __forceinline__ void pipe_tile(State& st, const char* stage, int qt0) {
+  static __device__ __forceinline__ void pipe_tile(const BwdArgs& a, State& st, const char* stage,
+                                                   int h, int qt0) {
     Pipe c;
     c.qc = stage;
     c.dc = stage + TL::BYTES;
     c.sc = stage + 2 * TL::BYTES;
     c.dlt = st.key - qt0 - 4 * st.hl;
     c.msk = qt0 < st.kw0 + 31;
+    c.qt0 = qt0;
+    if (MASK) {
+      c.mcol = a.mask + st.b * a.m_sb + h * a.m_sh + min(st.key, a.Nk - 1);
+      c.msq = a.m_sq;
+    }
     pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
     pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
 
-  // Iteration t over (head, q-tile) pairs: tile t (rows qt0..) is in `cur`,
-  // tile t+1 (head hn, rows qn..) goes into `nxt`.
-  static __device__ __forceinline__ void step(const BwdArgs& a, State& st, int t, int n_t, int qt0,
-                                              int hn, int qn, char* cur, char* nxt, bool live) {
+  // Iteration t over (head, q-tile) pairs: tile t (head hc, rows qt0..) is
+  // in `cur`, tile t+1 (head hn, rows qn..) goes into `nxt`.
+  static __device__ __forceinline__ void step(const BwdArgs& a, State& st, int t, int n_t, int hc,
+                                              int qt0, int hn, int qn, char* cur, char* nxt,
+                                              bool live) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 1 < n_t) issue(a, st, hn, qn, nxt);
@@ -730,7 +773,7 @@ struct BwdKV {
     if (CAUSAL && qt0 + BR - 1 < st.kw0) return;         // no row of the tile sees them
     // Keys at or past kv_limit are not masked here: a key's P and dS only
     // reach its own rows of dK / dV, which are stored as zero.
-    pipe_tile<PF>(st, cur, qt0);
+    pipe_tile<PF>(a, st, cur, hc, qt0);
   }
 
   static __device__ void run(const BwdArgs& a, char* s0, char* s1) {
@@ -774,6 +817,7 @@ struct BwdKV {
       st.dv[dt] = f32x16{};
     }
     st.c = a.c;
+    st.nq1 = a.Nq - 1;
     st.q0p = (const char*)((const _Float16*)a.q16 + b * a.q_sb);
     st.d0p = (const char*)((const _Float16*)a.do16 + b * a.q_sb);
     st.head_bytes = a.q_sh * 2;
@@ -795,7 +839,7 @@ struct BwdKV {
 
     // tiles walk the (head, q-tile) pairs head-major; tile t is in stage t % 2
     if (n_t > 0) issue(a, st, h0, q_start, s0);
-    int q0 = q_start;              // rows of tile t
+    int hc = h0, q0 = q_start;     // head and rows of tile t
     int hn = h0, qn = q_start;     // head and rows of tile t + 1
     for (int t = 0; t < n_t; t += 2) {
       qn += BR;
@@ -803,7 +847,8 @@ struct BwdKV {
         qn = q_start;
         ++hn;
       }
-      step(a, st, t, n_t, q0, hn, qn, s0, s1, live);
+      step(a, st, t, n_t, hc, q0, hn, qn, s0, s1, live);
+      hc = hn;
       q0 = qn;
       if (t + 1 >= n_t) break;
       qn += BR;
@@ -811,7 +856,8 @@ struct BwdKV {
         qn = q_start;
         ++hn;
       }
-      step(a, st, t + 1, n_t, q0, hn, qn, s1, s0, live);
+      step(a, st, t + 1, n_t, hc, q0, hn, qn, s1, s0, live);
+      hc = hn;
       q0 = qn;
     }
 
@@ -846,9 +892,9 @@ struct BwdKV {
   }
 };
 
-template <class E, int D, int NW, int BR, bool CAUSAL>
+template <class E, int D, int NW, int BR, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
-  using K = BwdKV<E, D, NW, BR, CAUSAL>;
+  using K = BwdKV<E, D, NW, BR, CAUSAL, MASK>;
   __shared__ __attribute__((aligned(1024))) char s0[K::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s1[K::STAGE_BYTES];
   K::run(a, s0, s1);

@@ -49,6 +49,8 @@ struct BwdArgs {
   float* part_dk;        // [kv_chunks, B, Hkv, Nk, d] workspace (kv_chunks > 1)
   float* part_dv;
   const int32_t* kv_lens;
+  const float* mask;     // optional additive mask, element (b,h,i,j) at
+  int64_t m_sb, m_sh, m_sq;   // mask[b*m_sb + h*m_sh + i*m_sq + j]
   int64_t q_sb, q_sh, q_sn;   // q, o, dout, dq share these
   int64_t k_sb, k_sh, k_sn;   // k, v, dk, dv share these
   int32_t B, Hq, Hkv, Nq, Nk, d;

@@ -127,8 +127,9 @@ size_t attn_bwd_workspace_bytes(const attn_params* p);
  *   grad_dtype: element type of dq, dk, dv: ATTN_FP32 or p->dtype
  *   workspace: device memory of at least attn_bwd_workspace_bytes(p) bytes,
  *              16-byte aligned; its contents on entry do not matter.
- * The additive mask is not supported by the backward (ATTN_EUNSUPPORTED);
- * kv_lens and causal are.  The result is deterministic: no atomics. */
+ * The additive mask (p->mask, the same one the forward took), kv_lens and
+ * causal are all supported; fp32 inputs are not (ATTN_EUNSUPPORTED).  The
+ * result is deterministic: no atomics. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,

@@ -68,11 +68,13 @@ def test_validate_rejects(kw, code):
 
 def test_validate_backward_limits():
     assert bd.attn_validate(_p(dtype=bd.ATTN_FP32), True) == bd.ATTN_EUNSUPPORTED
+    # the additive mask is supported by both passes; negative strides are not
     p = _p(mask_ptr=16, mask_strides=(0, 0, 64))
     assert bd.attn_validate(p, False) == bd.ATTN_OK
-    assert bd.attn_validate(p, True) == bd.ATTN_EUNSUPPORTED
+    assert bd.attn_validate(p, True) == bd.ATTN_OK
     p = _p(mask_ptr=16, mask_strides=(0, -1, 64))
     assert bd.attn_validate(p, False) == bd.ATTN_EINVAL
+    assert bd.attn_validate(p, True) == bd.ATTN_EINVAL
     assert bd.attn_validate(_p(d=48), True) == bd.ATTN_OK
 
 

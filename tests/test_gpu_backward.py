@@ -25,15 +25,17 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run(w, x, *, layout="bhnd", causal=False, scale=None, grad_dtype="fp32"):
+def _run(w, x, *, layout="bhnd", causal=False, scale=None, grad_dtype="fp32", mask=None):
     import torch
     from exact_attention_25_amd import binding as bd
     t = {n: to_device(to_layout(x[n + "_raw"], layout), w.dtype) for n in ("q", "k", "v", "do")}
     lens = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).cuda()
+    m = None if mask is None else torch.from_numpy(mask.astype(np.float32)).cuda()
     o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], layout=layout, causal=causal, scale=scale,
-                         kv_lens=lens)
+                         attn_mask=m, kv_lens=lens)
     dq, dk, dv = bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], layout=layout,
-                             causal=causal, scale=scale, kv_lens=lens, grad_dtype=grad_dtype)
+                             causal=causal, scale=scale, attn_mask=m, kv_lens=lens,
+                             grad_dtype=grad_dtype)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -62,6 +64,52 @@ SMALL = [
     ("bf16_d96_causal", 1, 2, 2, 300, 300, 96, "bf16", True, None, "bhnd", None),
     ("fp16_many_heads_chunks", 1, 16, 1, 96, 96, 128, "fp16", True, None, "bhnd", None),
 ]
+
+
+# Additive masks in the backward (logit units, after scaling; -inf entries
+# exclude a key; strides 0 broadcast), alone and with causal and key lengths.
+MASKED = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mask kind, layout
+    ("bf16_mask_full_gqa", 2, 4, 2, 200, 170, 128, "bf16", False, None, "full", "bhnd"),
+    ("fp16_mask_keys_bcast_lens", 2, 2, 2, 150, 260, 64, "fp16", False, (100, 260), "keys", "bhnd"),
+    ("bf16_mask_causal_bnhd", 1, 4, 1, 300, 300, 128, "bf16", True, None, "rows11", "bnhd"),
+    ("fp16_mask_d40_dead_rows", 1, 2, 2, 96, 96, 40, "fp16", False, None, "dead_rows", "bhnd"),
+]
+
+
+def _bwd_mask(kind, B, Hq, Nq, Nk, rng):
+    if kind == "full":
+        m = rng.standard_normal((B, Hq, Nq, Nk)) * 2
+        m[:, :, :, ::9] = -np.inf
+    elif kind == "keys":                       # [B,1,1,Nk]: per-batch key bias, broadcast
+        m = np.zeros((B, 1, 1, Nk))
+        m[..., Nk // 2:] = -1e9
+        m[..., : Nk // 5] += rng.standard_normal(Nk // 5)
+    elif kind == "rows11":                     # [1,1,Nq,Nk]: one mask for every (b, h)
+        m = rng.standard_normal((1, 1, Nq, Nk))
+        m[0, 0, :, 5::11] = -np.inf
+    elif kind == "dead_rows":                  # rows whose every key is masked
+        m = np.zeros((1, 1, Nq, Nk))
+        m[0, 0, 3] = -np.inf
+        m[0, 0, 40] = -np.inf
+    else:
+        raise ValueError(kind)
+    return m.astype(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[c[0] for c in MASKED])
+def test_backward_additive_mask(gpu_lib, case):
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mkind, layout = case
+    _say(f"[bwd-mask] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens, with_do=True)
+    mask = _bwd_mask(mkind, B, Hq, Nq, Nk, np.random.default_rng(11))
+    dq, dk, dv = _run(w, x, layout=layout, causal=causal, mask=mask)
+    dQ, dK, dV, _, _ = ref_bwd(x["q"], x["k"], x["v"], x["do"], causal=causal, mask=mask,
+                               kv_lens=x["kv_lens"])
+    _check(name + " dq", from_layout(host(dq), layout), dQ)
+    _check(name + " dk", from_layout(host(dk), layout), dK)
+    _check(name + " dv", from_layout(host(dv), layout), dV)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
