@@ -39,7 +39,6 @@ attn_status attn_validate(const attn_params* p, int for_backward) {
   if (p->causal && p->Nq != p->Nk) return ATTN_EINVAL;
   if (p->mask && (p->mask_sb < 0 || p->mask_sh < 0 || p->mask_sq < 0)) return ATTN_EINVAL;
   if (p->d < 8 || p->d > 128 || p->d % 8 != 0) return ATTN_EUNSUPPORTED;
-  if (for_backward && p->dtype == ATTN_FP32) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -99,7 +98,8 @@ struct BwdWorkspace {
 
 BwdWorkspace bwd_workspace(const attn_params* p) {
   BwdWorkspace w;
-  w.chunks = attn::bwd_kv_chunks(p->B, p->Hkv, p->Nk, p->Hq / p->Hkv);
+  // the fp32 dK/dV kernel sums all q-heads of a kv-head itself (no partials)
+  w.chunks = p->dtype == ATTN_FP32 ? 1 : attn::bwd_kv_chunks(p->B, p->Hkv, p->Nk, p->Hq / p->Hkv);
   w.ld = (p->Nq + 127) / 128 * 128;
   w.rows = align256((size_t)p->B * p->Hq * w.ld * sizeof(float));
   w.part = w.chunks > 1 ? align256((size_t)w.chunks * p->B * p->Hkv * p->Nk * p->d * sizeof(float)) : 0;
@@ -171,7 +171,9 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.c = a.scale * 1.4426950408889634f;
   a.grad_f32 = grad_dtype == ATTN_FP32 ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = attn::launch_bwd16(a, p->dtype == ATTN_BF16, p->causal != 0, s);
+  const hipError_t e = p->dtype == ATTN_FP32
+                           ? attn::launch_bwd32(a, p->causal != 0, s)
+                           : attn::launch_bwd16(a, p->dtype == ATTN_BF16, p->causal != 0, s);
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 

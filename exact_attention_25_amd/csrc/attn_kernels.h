@@ -69,5 +69,7 @@ int bwd_kv_chunks(int B, int Hkv, int Nk, int group);
 hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, bool causal, bool mask, hipStream_t st);
 hipError_t launch_fwd32(const FwdArgs& a, bool causal, bool mask, hipStream_t st);
 hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, bool causal, hipStream_t st);
+// fp32 backward (attn_bwd32.hip): D from dO and O, then dQ and dK/dV on the fp32 MFMA.
+hipError_t launch_bwd32(const BwdArgs& a, bool causal, hipStream_t st);
 
 }  // namespace attn

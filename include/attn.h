@@ -110,9 +110,10 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
 /* Bytes of device workspace attn_bwd needs for *p (0 if p is invalid): two
- * [B, Hq, Nq rounded up to 128] float arrays (D and -LSE*log2(e)); when the
- * q-heads of a kv-head are split over several work-groups, fp32 partial dK
- * and dV sums; for bf16 inputs, fp16 copies of q, dout and k. */
+ * [B, Hq, Nq rounded up to 128] float arrays (D and -LSE*log2(e)); for
+ * 16-bit inputs whose q-heads of a kv-head are split over several
+ * work-groups, fp32 partial dK and dV sums; for bf16 inputs, fp16 copies of
+ * q, dout and k. */
 size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /* Backward pass: gradients of <dout, O> with O = attention(q, k, v), with the
@@ -127,9 +128,9 @@ size_t attn_bwd_workspace_bytes(const attn_params* p);
  *   grad_dtype: element type of dq, dk, dv: ATTN_FP32 or p->dtype
  *   workspace: device memory of at least attn_bwd_workspace_bytes(p) bytes,
  *              16-byte aligned; its contents on entry do not matter.
- * The additive mask (p->mask, the same one the forward took), kv_lens and
- * causal are all supported; fp32 inputs are not (ATTN_EUNSUPPORTED).  The
- * result is deterministic: no atomics. */
+ * The additive mask (p->mask, the same one the forward took), kv_lens,
+ * causal and all three dtypes are supported (fp32 inputs take an all-fp32
+ * path).  The result is deterministic: no atomics. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,

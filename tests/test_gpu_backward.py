@@ -112,6 +112,43 @@ def test_backward_additive_mask(gpu_lib, case):
     _check(name + " dv", from_layout(host(dv), layout), dV)
 
 
+# fp32 inputs: every product in fp32 (fp32 MFMA), held to the fp32 bar of
+# 1e-5, taken relative to the gradient's own scale: max-abs error
+# <= 1e-5 * max(1, max |ref|).  Gradients reach |dQ| ~ 10 where the logits
+# are sharp (scale * |q||k| large), and there 1e-5 absolute is ~10 fp32 ulps
+# of the largest element, below what any fp32 order of summation reaches.
+# The relative-RMS bound is 3e-6: S itself is an fp32 sum of d products of
+# size up to ~40 (about 2e-5 absolute), i.e. up to ~6e-6 relative in P at
+# scale 0.3 and d = 128.
+TOL_F32 = 1e-5
+REL_RMS_F32 = 3e-6
+FP32 = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mask kind, layout, scale
+    ("fp32_tiny_workload_shape", 1, 2, 2, 128, 128, 64, "fp32", False, None, None, "bhnd", 0.125),
+    ("fp32_causal_gqa_lens", 2, 4, 2, 150, 150, 64, "fp32", True, (60, 150), None, "bhnd", None),
+    ("fp32_d128_bnhd_ragged", 1, 2, 2, 130, 97, 128, "fp32", False, None, None, "bnhd", 0.3),
+    ("fp32_d40_mask", 1, 2, 1, 100, 120, 40, "fp32", False, None, "full", "bhnd", None),
+    ("fp32_causal_mask_dead_rows", 1, 2, 2, 96, 96, 96, "fp32", True, None, "dead_rows", "bhnd", None),
+]
+
+
+@pytest.mark.parametrize("case", FP32, ids=[c[0] for c in FP32])
+def test_backward_fp32(gpu_lib, case):
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mkind, layout, scale = case
+    _say(f"[bwd-fp32] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens, with_do=True)
+    mask = None if mkind is None else _bwd_mask(mkind, B, Hq, Nq, Nk, np.random.default_rng(12))
+    dq, dk, dv = _run(w, x, layout=layout, causal=causal, scale=scale, mask=mask)
+    dQ, dK, dV, _, _ = ref_bwd(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=scale,
+                               mask=mask, kv_lens=x["kv_lens"])
+    for lbl, got, ref in ((" dq", dq, dQ), (" dk", dk, dK), (" dv", dv, dV)):
+        scale_ref = max(1.0, float(np.abs(ref).max()) if ref.size else 0.0)
+        mx = _check(name + lbl, from_layout(host(got), layout), ref, tol=TOL_F32 * scale_ref,
+                    rel=REL_RMS_F32)
+        _say(f"  {lbl.strip()}: max-abs {mx:.2e}, max|ref| {scale_ref:.2f}")
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_small(gpu_lib, case):
     name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, layout, scale = case
