@@ -248,8 +248,9 @@ def main():
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch size (counter runs whose per-dispatch "
                          "cycle counts must stay below 2^31); the JSON line then names the new B")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward (default) or the backward from the forward's O/LSE")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="time the forward (default), the backward from the forward's O/LSE, "
+                         "or the split-KV decode (attn_decode; --workload a decode workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the attention of every (batch, head) is "
@@ -293,7 +294,16 @@ def main():
         del src, dst
 
     fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"])
-    if bwd:
+    dec = args.which == "decode"
+    if dec:
+        dws = torch.empty(bd.attn_decode_workspace_bytes(bd.make_params(
+            w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, bd.ATTN_BF16 if w.dtype == "bf16" else bd.ATTN_FP16,
+            causal=w.causal)), dtype=torch.uint8, device=device)
+        fn = lambda: bd.attn_decode(t["q"], t["k"], t["v"], causal=w.causal,
+                                    kv_lens=t["kv_lens"], workspace=dws)
+        flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False)
+        dec_bytes = acc.decode_min_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.dtype, x["kv_lens"])
+    elif bwd:
         o, lse = fwd()
         ws = torch.empty(bd.attn_bwd_workspace_bytes(bd.make_params(
             w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, bd.ATTN_BF16 if w.dtype == "bf16" else bd.ATTN_FP16,
@@ -311,6 +321,44 @@ def main():
 
     tflops = flops / ms / 1e9
     peak = acc.PEAK_TFLOPS[w.dtype]
+    if dec:
+        gbs = dec_bytes / ms / 1e6
+        rec = {
+            "metric": "attention decode HBM GB/s (valid K/V cache read once, plus Q/O/LSE)",
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms, 4),
+            "ms_per_call_percentiles": pct,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w.dtype,
+            "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype})",
+            "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                       "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                       "key_padding": w.lens is not None, "pass": "decode"},
+            "pct_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS * 100, 2),
+            "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": acc.PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / acc.PEAK_HBM_GBS, 4),
+                         "traffic": None,
+                         "kernel": "attn::decode_split_kernel + attn::decode_merge_kernel, "
+                                   "one call per step"},
+        }
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+            cb = cpu_baseline(w, x)
+            # the oracle's time in the same unit: bytes of the sampled heads over its time
+            frac = cb["value"] / max(tflops, 1e-30)
+            cb = {"value": round(gbs * frac, 4), "unit": "GB/s", "cores": cb["cores"],
+                  "kind": "oracle", "sample": cb["sample"] + "; converted to GB/s at the decode's "
+                  "bytes per FLOP"}
+            rec["cpu_baseline"] = cb
+        print(json.dumps(rec), flush=True)
+        return
     rec = {
         "metric": METRIC if not bwd else "attention bwd TFLOPS (10*B*H*N^2*d, halved for causal)",
         "value": round(tflops, 2),

@@ -62,6 +62,17 @@ def bwd_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, grad_bytes=4) -> int:
             + B * Hkv * Nk * d * grad_bytes * 2)  # dK, dV out
 
 
+def decode_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, kv_lens=None) -> int:
+    """Minimum traffic of a decode call: the valid part of the K/V cache read
+    once (kv_lens[b] entries of batch b, or Nk), Q read, O and LSE written."""
+    e = ELEM_BYTES[dtype]
+    lens = [Nk] * B if kv_lens is None else [min(max(int(x), 0), Nk) for x in kv_lens]
+    return (sum(lens) * Hkv * d * e * 2      # K, V in (valid entries)
+            + B * Hq * Nq * d * e * 2        # Q in, O out
+            + B * Hq * Nq * 4                # LSE out
+            + (B * 4 if kv_lens is not None else 0))
+
+
 def score_matrix_bytes(B, H, N, elem_bytes=4) -> int:
     """Size of a materialised [B, H, N, N] score matrix."""
     return B * H * N * N * elem_bytes

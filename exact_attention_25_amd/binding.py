@@ -19,7 +19,7 @@ ATTN_FP32, ATTN_FP16, ATTN_BF16 = 0, 1, 2
 ATTN_BHND, ATTN_BNHD = 0, 1
 
 EXPORTS = ("attn_validate", "attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_status_string")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
 
 
 class AttnParams(ctypes.Structure):
@@ -62,6 +62,10 @@ def load():
     lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                              ctypes.c_size_t, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_decode_workspace_bytes.argtypes = [P]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_decode.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -91,6 +95,10 @@ def attn_validate(params: AttnParams, for_backward: bool = False) -> int:
 
 def attn_bwd_workspace_bytes(params: AttnParams) -> int:
     return int(load().attn_bwd_workspace_bytes(ctypes.byref(params)))
+
+
+def attn_decode_workspace_bytes(params: AttnParams) -> int:
+    return int(load().attn_decode_workspace_bytes(ctypes.byref(params)))
 
 
 # ----------------------------------------------------------------- torch side
@@ -212,6 +220,40 @@ def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, 
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_decode(q, k, v, *, layout="bhnd", causal=False, scale=None, kv_lens=None,
+                workspace=None, out=None, lse=None):
+    """Split-KV decode: Nq new queries against the k/v cache.  Returns (o, lse).
+
+    q: [B,Hq,Nq,d] ("bhnd") or [B,Nq,Hq,d] ("bnhd"); k, v: the cache with Hkv
+    heads and Nk entries.  kv_lens: optional int32 [B] device tensor of valid
+    cache entries.  causal: query i sees keys j <= L - Nq + i.
+    """
+    torch = _torch()
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
+    lens_ptr = None
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
+            raise ValueError("kv_lens must be an int32 device tensor with B entries")
+        kv_lens = kv_lens.contiguous()
+        lens_ptr = kv_lens.data_ptr()
+    p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
+                    causal, None, (0, 0, 0), lens_ptr)
+    need = attn_decode_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                         _stream_ptr(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode")
+    return out, lse
 
 
 def default_scale(d: int) -> float:

@@ -177,6 +177,85 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation of a decode call: attn_validate's rules, except that causal
+// (bottom-right aligned) does not need Nq == Nk; 16-bit dtypes, no mask.
+attn_status validate_decode(const attn_params* p) {
+  if (!p) return ATTN_EINVAL;
+  attn_params c = *p;
+  c.causal = 0;
+  const attn_status st = attn_validate(&c, 0);
+  if (st != ATTN_OK) return st;
+  if (p->dtype == ATTN_FP32 || p->mask) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+struct DecodeWorkspace {
+  int split_keys, n_splits;
+  size_t part_o, total;
+};
+
+DecodeWorkspace decode_workspace(const attn_params* p) {
+  DecodeWorkspace w;
+  const int rows = (p->Hq / p->Hkv) * p->Nq;
+  attn::decode_split(p->B, p->Hkv, rows, p->Nk, &w.split_keys, &w.n_splits);
+  const size_t nrow = (size_t)p->B * p->Hq * p->Nq;
+  w.part_o = align256((size_t)w.n_splits * nrow * p->d * sizeof(float));
+  w.total = w.part_o + align256((size_t)w.n_splits * nrow * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(const attn_params* p) {
+  if (validate_decode(p) != ATTN_OK) return 0;
+  const size_t t = decode_workspace(p).total;
+  return t > 0 ? t : 256;
+}
+
+attn_status attn_decode(const attn_params* p, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const attn_status st = validate_decode(p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Nq == 0) return ATTN_OK;
+  if (!q || !o || !lse) return ATTN_EINVAL;
+  if (p->Nk > 0 && (!k || !v)) return ATTN_EINVAL;
+  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return ATTN_EALIGN;
+  if (p->kv_lens && (reinterpret_cast<uintptr_t>(p->kv_lens) & 3u)) return ATTN_EALIGN;
+  if (!workspace || workspace_bytes < attn_decode_workspace_bytes(p)) return ATTN_EWORKSPACE;
+
+  const DecodeWorkspace ws = decode_workspace(p);
+  attn::DecodeArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.kv_lens = p->kv_lens;
+  char* wsp = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(wsp);
+  a.part_lse = reinterpret_cast<float*>(wsp + ws.part_o);
+  const Strides sq = strides_for(p->layout, p->Hq, p->Nq, p->d);
+  const Strides sk = strides_for(p->layout, p->Hkv, p->Nk, p->d);
+  a.q_sb = sq.sb; a.q_sh = sq.sh; a.q_sn = sq.sn;
+  a.k_sb = sk.sb; a.k_sh = sk.sh; a.k_sn = sk.sn;
+  a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.d = p->d;
+  a.group = p->Hq / p->Hkv;
+  a.rows = a.group * p->Nq;
+  a.n_rb = (a.rows + 31) / 32;
+  a.split_keys = ws.split_keys;
+  a.n_splits = ws.n_splits;
+  a.causal = p->causal ? 1 : 0;
+  a.c = resolve_scale(p) * 1.4426950408889634f;
+  const hipError_t e = attn::launch_decode(a, p->dtype == ATTN_BF16,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
 const char* attn_status_string(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ok";

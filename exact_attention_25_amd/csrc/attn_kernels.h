@@ -59,8 +59,39 @@ struct BwdArgs {
   float c;               // scale * log2(e)
   int32_t grad_f32;      // 1: dq/dk/dv are fp32, 0: input dtype
   int32_t kv_chunks;     // q-head chunks per kv-head in the dK/dV pass
-  int32_t ld_rows;       // row stride of delta / nl2 per (b, h): Nq rounded up to 64
+  int32_t ld_rows;       // row stride of delta / nl2 per (b, h): Nq rounded up to 128
 };
+
+// Kernel arguments of the split-KV decode (attn_decode.hip).  The Nq new
+// queries of the `group` q-heads that share a kv-head are stacked into
+// rows = group * Nq rows (row r: q-head g*group + r / Nq, query r % Nq), and
+// the keys are cut into n_splits ranges of split_keys keys; each (batch,
+// kv-head, 32-row block, key range) yields a partial O and LSE, which the
+// merge kernel combines.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_lens;
+  float* part_o;         // [n_splits, B, Hq, Nq, d] fp32 (workspace)
+  float* part_lse;       // [n_splits, B, Hq, Nq] fp32 (workspace)
+  int64_t q_sb, q_sh, q_sn;   // q and o share these
+  int64_t k_sb, k_sh, k_sn;   // k and v share these
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t group;         // Hq / Hkv
+  int32_t rows;          // group * Nq
+  int32_t n_rb;          // 32-row blocks: ceil(rows / 32)
+  int32_t split_keys;    // keys per split (a multiple of 32)
+  int32_t n_splits;      // ceil(Nk / split_keys)
+  int32_t causal;        // 1: query i sees keys j <= L - Nq + i (L = the batch's key count)
+  float c;               // scale * log2(e)
+};
+
+// Split of the decode's keys, shared by the workspace sizing and the launch.
+void decode_split(int B, int Hkv, int rows, int Nk, int* split_keys, int* n_splits);
+hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, hipStream_t st);
 
 // Work split of the backward, shared by the workspace sizing and the launch.
 constexpr int kBwdKeysPerBlock = 128;   // keys per dK/dV work-group

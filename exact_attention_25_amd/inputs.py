@@ -57,6 +57,10 @@ WORKLOADS = {
         Workload("long_bf16_b8_h32_n4096_d128", 8, 32, 32, 4096, 4096, 128, "bf16", 4),
         Workload("causal_gqa_bf16_b4_h32_kv2_n8192_d128", 4, 32, 2, 8192, 8192, 128, "bf16", 5,
                  causal=True, lens=(4096, 8192), backward=True),
+        # decode: one new token per sequence against a 32K key/value cache whose
+        # valid lengths vary over the batch (served with attn_decode)
+        Workload("decode_bf16_b8_hq32_kv8_q1_nk32768_d128", 8, 32, 8, 1, 32768, 128, "bf16", 6,
+                 lens=(16384, 32768)),
     ]
 }
 

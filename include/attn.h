@@ -137,6 +137,30 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      attn_dtype grad_dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_decode needs for *p (0 if p is not a valid
+ * decode problem): the fp32 partial outputs and log-sum-exps of the key
+ * splits, [n_splits, B, Hq, Nq, d] and [n_splits, B, Hq, Nq]. */
+size_t attn_decode_workspace_bytes(const attn_params* p);
+
+/* Decode attention: a few new queries (Nq, typically 1..16) against a long
+ * key/value cache, split over the keys and merged through the log-sum-exp
+ * (FlashDecoding; FlashAttention技术解析 §5.2, decode phase).  Computes the
+ * same O and LSE as attn_fwd for:
+ *   q: [B,Hq,Nq,d] / [B,Nq,Hq,d]; k, v: [B,Hkv,Nk,d] / [B,Nk,Hkv,d] (the
+ *      cache); o: q's shape; lse: [B,Hq,Nq] fp32
+ *   kv_lens: optional per-batch count of valid cache entries
+ *   causal: the Nq queries are the last Nq positions of the sequence: query
+ *      i sees keys j <= L - Nq + i, with L = kv_lens[b] (or Nk).  Unlike
+ *      attn_fwd, Nq may differ from Nk.
+ * 16-bit dtypes only and no additive mask (ATTN_EUNSUPPORTED otherwise);
+ * other parameters as for attn_fwd.
+ *   workspace: device memory of at least attn_decode_workspace_bytes(p)
+ *              bytes, 16-byte aligned; its contents on entry do not matter.
+ * Deterministic: the splits are merged in a fixed order. */
+attn_status attn_decode(const attn_params* p, const void* q, const void* k,
+                        const void* v, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status s);
 

@@ -59,3 +59,16 @@ def check_out(o_gpu, lse_gpu, O_ref, L_ref, dtype, label=""):
         ltol = (1e-5 if dtype == "fp32" else 1e-4) + 1e-6 * float(np.abs(L_ref[~dead]).max())
         assert float(lerr.max()) <= ltol, f"{label}: LSE max-abs {lerr.max():.3e}"
     return max_abs
+
+
+def decode_causal_mask(B, Nq, Nk, kv_lens=None):
+    """Additive [B,1,Nq,Nk] mask of decode's causal rule: the Nq queries are the
+    last Nq positions of a sequence of L = kv_lens[b] (or Nk) keys, so query i
+    sees keys j <= L - Nq + i.  Keys at or past L are left to kv_lens."""
+    m = np.zeros((B, 1, Nq, Nk))
+    j = np.arange(Nk)[None, :]
+    for b in range(B):
+        L = Nk if kv_lens is None else int(min(max(kv_lens[b], 0), Nk))
+        lim = L - Nq + np.arange(Nq)[:, None]
+        m[b, 0][j > lim] = -np.inf
+    return m

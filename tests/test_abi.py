@@ -116,3 +116,25 @@ def test_status_strings():
         assert t and t not in seen
         seen.add(t)
     assert bd.attn_status_string(99) == "unknown status"
+
+
+def test_decode_validation_and_errors():
+    lib = bd.load()
+    # causal decode does not need Nq == Nk (the queries are the last Nq positions)
+    p = _p(d=128)
+    p.Nq, p.Nk, p.causal = 1, 4096, 1
+    need = bd.attn_decode_workspace_bytes(p)
+    assert need > 0 and need % 256 == 0
+    q = _p(dtype=bd.ATTN_FP32)
+    assert bd.attn_decode_workspace_bytes(q) == 0
+    m = _p(mask_ptr=16, mask_strides=(0, 0, 64))
+    assert bd.attn_decode_workspace_bytes(m) == 0
+    args = [16] * 5
+    assert lib.attn_decode(ctypes.byref(q), *args, 16, 1 << 30, None) == bd.ATTN_EUNSUPPORTED
+    assert lib.attn_decode(ctypes.byref(m), *args, 16, 1 << 30, None) == bd.ATTN_EUNSUPPORTED
+    assert lib.attn_decode(ctypes.byref(p), *args, 16, need - 1, None) == bd.ATTN_EWORKSPACE
+    assert lib.attn_decode(ctypes.byref(p), *args, None, need, None) == bd.ATTN_EWORKSPACE
+    args[0] = 8
+    assert lib.attn_decode(ctypes.byref(p), *args, 16, need, None) == bd.ATTN_EALIGN
+    bad = _p(d=44)
+    assert lib.attn_decode(ctypes.byref(bad), *([16] * 5), 16, 1 << 30, None) == bd.ATTN_EUNSUPPORTED

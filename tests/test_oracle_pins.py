@@ -287,3 +287,32 @@ def test_tiled_online_softmax_equals_full_softmax(trial):
             np.testing.assert_array_equal(np.isneginf(Lt), np.isneginf(L))
             fin = np.isfinite(L)
             np.testing.assert_allclose(Lt[fin], L[fin], atol=1e-12, rtol=0)
+
+
+def test_decode_causal_rule_is_last_rows_of_causal_attention():
+    """Decode's causal rule (query i of the last Nq sees keys j <= L - Nq + i)
+    applied through an additive mask equals the last Nq rows of ordinary causal
+    attention over the whole sequence; with key lengths, equals the same over
+    the first L keys."""
+    from tests.gpu_util import decode_causal_mask
+    rng = np.random.default_rng(21)
+    B, H, N, d, Nq = 2, 3, 37, 16, 5
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    O_full, L_full = ref_fwd(q, k, v, causal=True)
+    m = decode_causal_mask(B, Nq, N)
+    O_dec, L_dec = ref_fwd(q[:, :, N - Nq:], k, v, mask=m)
+    np.testing.assert_allclose(O_dec, O_full[:, :, N - Nq:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L_dec, L_full[:, :, N - Nq:], rtol=0, atol=1e-12)
+    # key lengths: batch b has only its first L_b keys; its decode queries are
+    # its positions L_b - Nq .. L_b - 1
+    lens = np.array([20, 37], dtype=np.int32)
+    m = decode_causal_mask(B, Nq, N, lens)
+    qd = np.stack([q[b, :, lens[b] - Nq:lens[b]] for b in range(B)])
+    O_dec, L_dec = ref_fwd(qd, k, v, mask=m, kv_lens=lens)
+    for b in range(B):
+        Lb = int(lens[b])
+        O_b, L_b = ref_fwd(q[b:b + 1, :, :Lb], k[b:b + 1, :, :Lb], v[b:b + 1, :, :Lb], causal=True)
+        np.testing.assert_allclose(O_dec[b], O_b[0, :, Lb - Nq:], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L_dec[b], L_b[0, :, Lb - Nq:], rtol=0, atol=1e-12)
