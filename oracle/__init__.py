@@ -23,5 +23,8 @@ from .attention_ref import (  # noqa: F401
     ref_fwd_rows,
     ref_bwd,
     ref_bwd_group,
+    query_positions,
+    local_visible,
+    softcap_logits,
 )
 from .tiled_model import tiled_fwd  # noqa: F401

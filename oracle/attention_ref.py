@@ -34,6 +34,27 @@ design notes of the repository):
 * LSE is the natural-log log-sum-exp of the scaled, masked logits;
 * grouped-query attention: q-head h reads kv-head h // (Hq / Hkv);
 * dropout is absent (p = 0).
+
+Local masks and the score modification (all optional, off by default):
+
+* ``softcap``: the scaled logit s becomes cap * tanh(s / cap), before the
+  additive mask -- the tanh soft cap of the FlexAttention score_mod example
+  in the PyTorch attention-options article (atyun.com/61003), section
+  "Score Mod示例：使用Tanh进行软上限" (cap 30 there);
+* ``window=(left, right)``: key j is visible to the query at position p iff
+  p - left <= j <= p + right, a negative bound leaving its side open -- the
+  ``window_size`` argument of flash_attn_func on the ChatGLM2-6B page, §3
+  step 3 (whose default (-1, -1) is no window);
+* ``grid=(cols, nbr_rows, nbr_cols)``: positions are cells of a row-major
+  grid with ``cols`` columns (p -> (p // cols, p % cols)), and key j is
+  visible iff its row and column differ from the query's by less than
+  nbr_rows and nbr_cols -- the neighbourhood mask_mod example of the same
+  PyTorch article, section "Mask Mod示例：邻域屏蔽" (56 x 56 patches, both
+  differences < 5);
+* positions: query row i sits at position p = i; with ``bottom_right`` the
+  Nq queries are the last Nq positions of the batch's L keys (L = kv_len or
+  Nk), p = L - Nq + i, the rule of a decode step.  Causal attention then
+  means j <= p, and does not need Nq == Nk.
 """
 from __future__ import annotations
 
@@ -78,28 +99,82 @@ def _group(hq: int, hkv: int) -> int:
     return hq // hkv
 
 
+def query_positions(nq, nk, *, kv_len=None, bottom_right=False, rows=None):
+    """Sequence positions of the query rows ``rows`` (default all Nq rows).
+
+    p = i, or with ``bottom_right`` p = L - Nq + i where L is the number of
+    valid keys (kv_len clamped to [0, Nk], else Nk).
+    """
+    ridx = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    if not bottom_right:
+        return ridx
+    L = nk if kv_len is None else int(min(max(int(kv_len), 0), nk))
+    return L - nq + ridx
+
+
+def local_visible(pos, nk, *, window=None, grid=None):
+    """[len(pos), Nk] boolean: which keys the sliding window and the 2-D
+    neighbourhood leave visible to queries at positions ``pos``.
+
+    window = (left, right): p - left <= j <= p + right; a negative bound is
+    open.  grid = (cols, nbr_rows, nbr_cols): |p//cols - j//cols| < nbr_rows
+    and |p%cols - j%cols| < nbr_cols.
+    """
+    pos = np.asarray(pos, dtype=np.int64)[:, None]
+    j = np.arange(nk, dtype=np.int64)[None, :]
+    vis = np.ones((pos.shape[0], nk), dtype=bool)
+    if window is not None:
+        left, right = (int(x) for x in window)
+        if left >= 0:
+            vis &= j >= pos - left
+        if right >= 0:
+            vis &= j <= pos + right
+    if grid is not None:
+        cols, nr, nc = (int(x) for x in grid)
+        if cols <= 0 or nr <= 0 or nc <= 0:
+            raise ValueError("grid needs cols, nbr_rows, nbr_cols > 0")
+        if np.any(pos < 0):
+            raise ValueError("grid positions must be >= 0")
+        vis &= np.abs(pos // cols - j // cols) < nr
+        vis &= np.abs(pos % cols - j % cols) < nc
+    return vis
+
+
+def softcap_logits(S, cap):
+    """cap * tanh(S / cap): the tanh soft cap (PyTorch attention-options
+    article, "Score Mod示例：使用Tanh进行软上限").  cap None or 0: S unchanged."""
+    if not cap:
+        return S
+    return cap * np.tanh(S / cap)
+
+
 def ref_scores(q_bh, k_bg, *, scale, mask_bh=None, kv_len=None, causal=False,
-               rows=None):
+               rows=None, softcap=None, window=None, grid=None, bottom_right=False):
     """Scaled, masked logits S for one (batch, head): an [Nq, Nk] fp64 array.
 
-    S = (Q K^T) * scale, then + mask, then keys j >= kv_len and (causal) keys
-    j > i set to -inf.  ``rows`` selects query rows (global indices), so a
+    S = (Q K^T) * scale, soft-capped if ``softcap``, then + mask, then keys
+    j >= kv_len, (causal) keys j > p and keys outside the window or the
+    neighbourhood set to -inf, p being the query's position (p = i unless
+    ``bottom_right``).  ``rows`` selects query rows (global indices), so a
     slab of S can be formed without the rest.
     """
     q_bh = np.asarray(q_bh, dtype=np.float64)
     k_bg = np.asarray(k_bg, dtype=np.float64)
     nq, nk = q_bh.shape[0], k_bg.shape[0]
     ridx = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
-    S = (q_bh[ridx] @ k_bg.T) * scale
+    pos = query_positions(nq, nk, kv_len=kv_len, bottom_right=bottom_right, rows=ridx)
+    S = softcap_logits((q_bh[ridx] @ k_bg.T) * scale, softcap)
     if mask_bh is not None:
         S = S + np.asarray(mask_bh, dtype=np.float64)[ridx]
     if kv_len is not None:
         L = int(min(max(int(kv_len), 0), nk))
         S[:, L:] = -np.inf
     if causal:
-        if nq != nk:
+        if nq != nk and not bottom_right:
             raise ValueError("causal attention needs Nq == Nk")
-        S[np.arange(nk)[None, :] > ridx[:, None]] = -np.inf
+        S[np.arange(nk)[None, :] > pos[:, None]] = -np.inf
+    if window is not None or grid is not None:
+        S[~local_visible(pos, nk, window=window, grid=grid)] = -np.inf
     return S
 
 
@@ -147,8 +222,19 @@ def _shapes(q, k, v):
     return B, Hq, Hkv, Nq, Nk, d
 
 
+_MODS = ("softcap", "window", "grid", "bottom_right")
+
+
+def _mods(mods):
+    """The local-mask / score-mod keywords (see the module docstring)."""
+    bad = set(mods) - set(_MODS)
+    if bad:
+        raise TypeError(f"unknown keyword(s) {sorted(bad)}")
+    return mods
+
+
 def ref_probs(q, k, *, scale=None, causal=False, mask=None, kv_lens=None,
-              layout="bhnd"):
+              layout="bhnd", **mods):
     """P = softmax(S) for every (b, h): [B, Hq, Nq, Nk] fp64 (small shapes)."""
     q = _to_bhnd(q, layout)
     k = _to_bhnd(k, layout)
@@ -163,18 +249,20 @@ def ref_probs(q, k, *, scale=None, causal=False, mask=None, kv_lens=None,
         for h in range(Hq):
             S = ref_scores(q[b, h], k[b, h // G], scale=s,
                            mask_bh=None if M is None else M[b, h],
-                           kv_len=None if L is None else L[b], causal=causal)
+                           kv_len=None if L is None else L[b], causal=causal,
+                           **_mods(mods))
             P[b, h], _ = _softmax_rows(S)
     return P
 
 
 def ref_fwd(q, k, v, *, scale=None, causal=False, mask=None, kv_lens=None,
-            layout="bhnd"):
+            layout="bhnd", **mods):
     """Attention forward: returns (O, LSE) in fp64.
 
     q: [B,Hq,Nq,d] (layout "bhnd") or [B,Nq,Hq,d] ("bnhd"); k, v likewise
     with Hkv heads and Nk keys.  mask: optional additive array broadcastable
-    to [B,Hq,Nq,Nk].  kv_lens: optional [B] valid key counts.
+    to [B,Hq,Nq,Nk].  kv_lens: optional [B] valid key counts.  ``mods``:
+    softcap, window, grid, bottom_right (module docstring).
     O has q's layout; LSE is [B,Hq,Nq].
 
     Per (b, h): S from :func:`ref_scores`, P by the two-pass softmax, O = P V,
@@ -196,7 +284,8 @@ def ref_fwd(q, k, v, *, scale=None, causal=False, mask=None, kv_lens=None,
             g = h // G
             S = ref_scores(q[b, h], k[b, g], scale=s,
                            mask_bh=None if M is None else M[b, h],
-                           kv_len=None if L is None else L[b], causal=causal)
+                           kv_len=None if L is None else L[b], causal=causal,
+                           **_mods(mods))
             P, lse = _softmax_rows(S)
             O[b, h] = P @ v[b, g]
             LSE[b, h] = lse
@@ -204,7 +293,7 @@ def ref_fwd(q, k, v, *, scale=None, causal=False, mask=None, kv_lens=None,
 
 
 def ref_fwd_rows(q, k, v, b, h, rows, *, scale=None, causal=False, mask=None,
-                 kv_lens=None, layout="bhnd"):
+                 kv_lens=None, layout="bhnd", **mods):
     """(O rows, LSE rows) of one head (b, h) for the query indices ``rows``.
 
     Rows of attention are independent, so a sample of rows of a large problem
@@ -220,13 +309,14 @@ def ref_fwd_rows(q, k, v, b, h, rows, *, scale=None, causal=False, mask=None,
     L = _lens_for(kv_lens, B)
     S = ref_scores(q[b, h], k[b, h // G], scale=s,
                    mask_bh=None if M is None else M[b, h],
-                   kv_len=None if L is None else L[b], causal=causal, rows=rows)
+                   kv_len=None if L is None else L[b], causal=causal, rows=rows,
+                   **_mods(mods))
     P, lse = _softmax_rows(S)
     return P @ v[b, h // G], lse
 
 
 def ref_bwd_group(q, k, v, do, b, g, *, scale=None, causal=False, mask=None,
-                  kv_lens=None, layout="bhnd"):
+                  kv_lens=None, layout="bhnd", **mods):
     """Exact backward for one batch b and one kv-head g (all its q-heads).
 
     Returns (dQ [G,Nq,d] for q-heads g*G..g*G+G-1, dK [Nk,d], dV [Nk,d],
@@ -240,7 +330,9 @@ def ref_bwd_group(q, k, v, do, b, g, *, scale=None, causal=False, mask=None,
         dS   = P * (dP - D)
         dQ   = s dS K,   dK += s dS^T Q,   dV += P^T dO
     summed over the q-heads that share kv-head g.  No gradient reaches the
-    mask.
+    mask.  With a soft cap the logit is cap * tanh(z / cap) of z = s q.k, so
+    dS is multiplied by its derivative 1 - tanh(z / cap)^2 before the
+    products with K and Q (chain rule).
     """
     q = _to_bhnd(q, layout)
     k = _to_bhnd(k, layout)
@@ -263,13 +355,18 @@ def ref_bwd_group(q, k, v, do, b, g, *, scale=None, causal=False, mask=None,
         h = g * G + r
         S = ref_scores(q[b, h], Kg, scale=s,
                        mask_bh=None if M is None else M[b, h],
-                       kv_len=None if L is None else L[b], causal=causal)
+                       kv_len=None if L is None else L[b], causal=causal,
+                           **_mods(mods))
         P, lse = _softmax_rows(S)
         Oh = P @ Vg
         dOh = do[b, h]
         D = np.sum(dOh * Oh, axis=1, keepdims=True)
         dP = dOh @ Vg.T
         dS = P * (dP - D)
+        cap = mods.get("softcap")
+        if cap:
+            # d/dz [cap tanh(z / cap)] = 1 - tanh(z / cap)^2 at z = s q.k
+            dS = dS * (1.0 - np.tanh((q[b, h] @ Kg.T) * s / cap) ** 2)
         dQ[r] = s * (dS @ Kg)
         dK += s * (dS.T @ q[b, h])
         dV += P.T @ dOh
@@ -279,7 +376,7 @@ def ref_bwd_group(q, k, v, do, b, g, *, scale=None, causal=False, mask=None,
 
 
 def ref_bwd(q, k, v, do, *, scale=None, causal=False, mask=None, kv_lens=None,
-            layout="bhnd"):
+            layout="bhnd", **mods):
     """Exact backward for the whole problem: returns (dQ, dK, dV, O, LSE).
 
     dQ/dK/dV/O come back in the input layout; LSE is [B,Hq,Nq].
@@ -298,7 +395,7 @@ def ref_bwd(q, k, v, do, *, scale=None, causal=False, mask=None, kv_lens=None,
         for g in range(Hkv):
             dq, dk, dv, o, lse = ref_bwd_group(
                 q, k, v, do, b, g, scale=scale, causal=causal, mask=mask,
-                kv_lens=kv_lens, layout=layout)
+                kv_lens=kv_lens, layout=layout, **mods)
             dQ[b, g * G:(g + 1) * G] = dq
             O[b, g * G:(g + 1) * G] = o
             LSE[b, g * G:(g + 1) * G] = lse

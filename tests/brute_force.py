@@ -10,21 +10,43 @@ o_ic = sum_j p_ij v_jc.
 import math
 
 
-def attention(q, k, v, scale, causal=False, mask=None, kv_len=None):
+def attention(q, k, v, scale, causal=False, mask=None, kv_len=None, softcap=None,
+              window=None, grid=None, last_positions=False):
     """q: list of Nq rows, k/v: lists of Nk rows (lists of floats).
 
     Returns (o rows, lse list).  mask: Nq x Nk list or None.
+
+    Local options: the query of row i sits at position p = i, or with
+    ``last_positions`` at the (L - Nq + i)-th of the L valid keys.  softcap:
+    logit -> softcap * tanh(logit / softcap) before the mask.  window =
+    (left, right): keys p - left .. p + right (a negative bound is open).
+    grid = (cols, nbr_rows, nbr_cols): token t is the cell (t // cols,
+    t % cols) of a row-major grid, and a key is visible when both its row
+    and its column are nearer than nbr_rows / nbr_cols to the query's.
     """
     nq, nk, d = len(q), len(k), len(q[0])
+    L = nk if kv_len is None else kv_len
     out, lses = [], []
     for i in range(nq):
+        p = (L - nq + i) if last_positions else i
         logits = []
         for j in range(nk):
             visible = True
             if kv_len is not None and j >= kv_len:
                 visible = False
-            if causal and j > i:
+            if causal and j > p:
                 visible = False
+            if window is not None:
+                if window[0] >= 0 and p - j > window[0]:
+                    visible = False
+                if window[1] >= 0 and j - p > window[1]:
+                    visible = False
+            if grid is not None:
+                cols, nr, nc = grid
+                pr, pc = divmod(p, cols)
+                jr, jc = divmod(j, cols)
+                if abs(pr - jr) >= nr or abs(pc - jc) >= nc:
+                    visible = False
             if not visible:
                 logits.append(None)
                 continue
@@ -32,6 +54,8 @@ def attention(q, k, v, scale, causal=False, mask=None, kv_len=None):
             for c in range(d):
                 dot += q[i][c] * k[j][c]
             x = dot * scale
+            if softcap:
+                x = softcap * math.tanh(x / softcap)
             if mask is not None:
                 x += mask[i][j]
             logits.append(x)
