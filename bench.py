@@ -17,7 +17,11 @@ oracle's backward on one (batch, kv-head) group.
 
 --extras also times the other workloads (the ViT, UNet self/cross, causal
 GQA forward and backward, and the long-context sweep) and adds them to the
-JSON line under "extras".  --copy-calibration runs a plain device copy of a
+JSON line under "extras".
+
+Workloads with a sliding window, a 2-D neighbourhood or a soft cap (the
+FlexAttention cases, e.g. vit_nbr_bf16_b8_h12_n3136_d64) pass them to the
+call; their FLOPs count 4*d per visible (query, key) pair and head.  --copy-calibration runs a plain device copy of a
 known size (for scaling HBM byte counters under rocprofv3).
 """
 from __future__ import annotations
@@ -43,13 +47,32 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_25_amd", "csrc", f)
                             "device_common.h", "attn_kernels.h")]
 
 
+def is_local(w) -> bool:
+    return bool(w.window or w.grid)
+
+
+def local_kw(w) -> dict:
+    """The window / grid / soft cap keywords of a workload's calls."""
+    return {"window_size": w.window or (-1, -1), "grid": w.grid, "softcap": w.softcap}
+
+
+def fwd_flops_of(w, kv_lens):
+    from exact_attention_25_amd import accounting as acc
+    if is_local(w):
+        return 4.0 * w.d * w.Hq * acc.local_pairs(w.Nq, kv_lens, w.B, w.causal, w.window, w.grid)
+    return acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+
+
 def fwd_kernel_name(w) -> str:
     """The forward kernel instance attn_fwd dispatches to for workload w
-    (mirrors the dispatch in attn_fwd.hip)."""
+    (mirrors the dispatch in attn_fwd.hip and attn_fwd_local.hip)."""
     D = 128 if w.d > 64 else 64
     if w.dtype == "fp32":
         return f"attn::fwd32_kernel<{D},...>"
     e = "BF16" if w.dtype == "bf16" else "FP16"
+    if is_local(w) or w.softcap:
+        return (f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal and not is_local(w)).lower()},"
+                f"mask=false,local={str(is_local(w)).lower()},softcap={str(bool(w.softcap)).lower()}>")
     if not w.causal and w.Nk >= 8 * 64:
         return f"attn::fwd_pipe_kernel<{e},{D},64>"
     return f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal).lower()},mask=false>"
@@ -138,9 +161,21 @@ def workload_inputs(w, device, with_do=False):
     return x, t
 
 
-def cpu_baseline(w, x, budget_s=15.0, backward=False):
+def local_config(w) -> dict:
+    out = {}
+    if w.window:
+        out["window_size"] = list(w.window)
+    if w.grid:
+        out["grid"] = {"cols": w.grid[0], "nbr_rows": w.grid[1], "nbr_cols": w.grid[2]}
+    if w.softcap:
+        out["softcap"] = w.softcap
+    return out
+
+
+def cpu_baseline(w, x, budget_s=15.0, backward=False, decode=False):
     """The fp64 oracle on (batch, head) pairs in order, until ~budget_s of CPU
-    time; returns a dict in the metric's unit (TFLOP/s)."""
+    time; returns a dict in the metric's unit (TFLOP/s).  decode: the queries
+    are the last positions of each batch's keys (the decode rule)."""
     from threadpoolctl import threadpool_info
     from exact_attention_25_amd import accounting as acc
     from oracle import ref_bwd_group, ref_fwd
@@ -162,18 +197,29 @@ def cpu_baseline(w, x, budget_s=15.0, backward=False):
         flops = acc.bwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
         what = "fp64 numpy oracle backward (incl. its forward)"
     else:
+        mods = {k: v for k, v in (("window", w.window), ("grid", w.grid),
+                                  ("softcap", w.softcap or None)) if v}
+        if decode:
+            mods["bottom_right"] = True
+        flops = 0.0
         for b in range(w.B):
+            lens = None if x["kv_lens"] is None else x["kv_lens"][b:b + 1]
+            if decode:
+                per_head = 4.0 * w.d * acc.decode_pairs(w.Nq, w.Nk, lens, 1, w.causal, w.window)
+            elif is_local(w):
+                per_head = 4.0 * w.d * acc.local_pairs(w.Nq, lens, 1, w.causal, w.window, w.grid)
+            else:
+                per_head = acc.fwd_flops(1, 1, w.Nq, w.Nk, w.d, w.causal)
             for h in range(w.Hq):
                 g = h // G
-                lens = None if x["kv_lens"] is None else x["kv_lens"][b:b + 1]
                 ref_fwd(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, g:g + 1],
-                        x["v"][b:b + 1, g:g + 1], causal=w.causal, kv_lens=lens)
+                        x["v"][b:b + 1, g:g + 1], causal=w.causal, kv_lens=lens, **mods)
                 done += 1
+                flops += per_head
                 if time.perf_counter() - t0 >= budget_s:
                     break
             if time.perf_counter() - t0 >= budget_s:
                 break
-        flops = acc.fwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
         what = "fp64 numpy oracle forward"
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
@@ -293,16 +339,21 @@ def main():
         print("[bench] copy calibration: 3 x 1 GiB device copies", file=sys.stderr, flush=True)
         del src, dst
 
-    fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"])
+    lkw = local_kw(w)
+    fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"], **lkw)
     dec = args.which == "decode"
     if dec:
         dws = torch.empty(bd.attn_decode_workspace_bytes(bd.make_params(
             w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, bd.ATTN_BF16 if w.dtype == "bf16" else bd.ATTN_FP16,
-            causal=w.causal)), dtype=torch.uint8, device=device)
+            causal=w.causal, window_size=lkw["window_size"], softcap=w.softcap)),
+            dtype=torch.uint8, device=device)
         fn = lambda: bd.attn_decode(t["q"], t["k"], t["v"], causal=w.causal,
-                                    kv_lens=t["kv_lens"], workspace=dws)
-        flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False)
-        dec_bytes = acc.decode_min_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.dtype, x["kv_lens"])
+                                    kv_lens=t["kv_lens"], window_size=lkw["window_size"],
+                                    softcap=w.softcap, workspace=dws)
+        flops = 4.0 * w.d * w.Hq * acc.decode_pairs(w.Nq, w.Nk, x["kv_lens"], w.B, w.causal,
+                                                    w.window)
+        dec_bytes = acc.decode_min_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.dtype, x["kv_lens"],
+                                         w.window[0] if w.window else -1)
     elif bwd:
         o, lse = fwd()
         ws = torch.empty(bd.attn_bwd_workspace_bytes(bd.make_params(
@@ -313,7 +364,7 @@ def main():
         flops = acc.bwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
     else:
         fn = fwd
-        flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+        flops = fwd_flops_of(w, x["kv_lens"])
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     ms, wall = time_calls(fn, args.steps, args.warmup, stream)
 
@@ -324,7 +375,7 @@ def main():
     if dec:
         gbs = dec_bytes / ms / 1e6
         rec = {
-            "metric": "attention decode HBM GB/s (valid K/V cache read once, plus Q/O/LSE)",
+            "metric": "attention decode HBM GB/s (visible K/V cache read once, plus Q/O/LSE)",
             "value": round(gbs, 1),
             "unit": "GB/s",
             "n_gpus": 1,
@@ -339,7 +390,8 @@ def main():
             "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype})",
             "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                        "Nk": w.Nk, "d": w.d, "causal": w.causal,
-                       "key_padding": w.lens is not None, "pass": "decode"},
+                       "key_padding": w.lens is not None, "pass": "decode",
+                       **local_config(w)},
             "pct_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS * 100, 2),
             "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": acc.PEAK_HBM_GBS,
@@ -350,7 +402,7 @@ def main():
         }
         if not args.no_cpu_baseline:
             print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-            cb = cpu_baseline(w, x)
+            cb = cpu_baseline(w, x, decode=True)
             # the oracle's time in the same unit: bytes of the sampled heads over its time
             frac = cb["value"] / max(tflops, 1e-30)
             cb = {"value": round(gbs * frac, 4), "unit": "GB/s", "cores": cb["cores"],
@@ -359,8 +411,15 @@ def main():
             rec["cpu_baseline"] = cb
         print(json.dumps(rec), flush=True)
         return
+    metric = METRIC
+    if bwd:
+        metric = "attention bwd TFLOPS (10*B*H*N^2*d, halved for causal)"
+    elif is_local(w):
+        metric = "attention fwd TFLOPS (4*d FLOPs per visible (query, key) pair and head)"
+    elif w.name != DEFAULT_WORKLOAD:
+        metric = "attention fwd TFLOPS (4*B*H*N^2*d, halved for causal)"
     rec = {
-        "metric": METRIC if not bwd else "attention bwd TFLOPS (10*B*H*N^2*d, halved for causal)",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -375,12 +434,12 @@ def main():
         "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype})",
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "Hkv": w.Hkv, "N": w.Nq,
                    "d": w.d, "causal": w.causal, "mask": None, "key_padding": w.lens is not None,
-                   "pass": "backward" if bwd else "forward"},
+                   "pass": "backward" if bwd else "forward", **local_config(w)},
         "pct_of_peak": round(tflops / peak * 100, 2),
         "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": None if bwd else recorded_traffic(),
+                     "traffic": None if (bwd or w.name != DEFAULT_WORKLOAD) else recorded_traffic(),
                      "kernel": ("attn::bwd_prep_kernel + attn::bwd_q_kernel + attn::bwd_kv_kernel (+ reduce), one call per step"
                                 if bwd else fwd_kernel_name(w) + " (one launch per step)")},
     }

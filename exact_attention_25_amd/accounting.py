@@ -45,6 +45,51 @@ def useful_pairs(Nq, Nk, kv_lens=None, causal=False, B=1) -> int:
     return tot
 
 
+def local_pairs(N, kv_lens=None, B=1, causal=False, window=None, grid=None) -> int:
+    """Visible (query, key) pairs of a self-attention of N positions summed
+    over the batch, under key padding, causal masking, a sliding window
+    (left, right; -1 = open) and a 2-D neighbourhood (cols, nbr_rows,
+    nbr_cols): the work a local forward must do, 4 d FLOPs per pair and head.
+    """
+    import numpy as np
+    lens = [N] * B if kv_lens is None else [min(max(int(x), 0), N) for x in kv_lens]
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    if causal:
+        wr = 0 if wr < 0 else min(wr, 0)
+    tot = 0
+    j = np.arange(N, dtype=np.int64)[None, :]
+    for L in lens:
+        for i0 in range(0, N, 512):
+            i = np.arange(i0, min(i0 + 512, N), dtype=np.int64)[:, None]
+            ok = j < L
+            if wl >= 0:
+                ok = ok & (j >= i - wl)
+            if wr >= 0:
+                ok = ok & (j <= i + wr)
+            if grid is not None:
+                c, nr, nc = (int(x) for x in grid)
+                ok = ok & (np.abs(i // c - j // c) < nr) & (np.abs(i % c - j % c) < nc)
+            tot += int(ok.sum())
+    return tot
+
+
+def decode_pairs(Nq, Nk, kv_lens=None, B=1, causal=False, window=None) -> int:
+    """Visible (query, key) pairs of a decode call summed over the batch: the
+    Nq queries sit at positions L - Nq + i of each batch's L keys."""
+    lens = [Nk] * B if kv_lens is None else [min(max(int(x), 0), Nk) for x in kv_lens]
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    if causal:
+        wr = 0 if wr < 0 else min(wr, 0)
+    tot = 0
+    for L in lens:
+        for i in range(Nq):
+            p = L - Nq + i
+            lo = 0 if wl < 0 else max(p - wl, 0)
+            hi = L - 1 if wr < 0 else min(p + wr, L - 1)
+            tot += max(hi - lo + 1, 0)
+    return tot
+
+
 def fwd_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, with_lens=False) -> int:
     e = ELEM_BYTES[dtype]
     return (B * Hq * Nq * d * e * 2          # Q in, O out
@@ -62,11 +107,15 @@ def bwd_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, grad_bytes=4) -> int:
             + B * Hkv * Nk * d * grad_bytes * 2)  # dK, dV out
 
 
-def decode_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, kv_lens=None) -> int:
-    """Minimum traffic of a decode call: the valid part of the K/V cache read
-    once (kv_lens[b] entries of batch b, or Nk), Q read, O and LSE written."""
+def decode_min_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, kv_lens=None, window_left=-1) -> int:
+    """Minimum traffic of a decode call: the visible part of the K/V cache
+    read once (kv_lens[b] entries of batch b, or Nk; with a bounded left
+    window only the last Nq + window_left of them), Q read, O and LSE
+    written."""
     e = ELEM_BYTES[dtype]
     lens = [Nk] * B if kv_lens is None else [min(max(int(x), 0), Nk) for x in kv_lens]
+    if window_left is not None and window_left >= 0:
+        lens = [min(L, Nq + int(window_left)) for L in lens]
     return (sum(lens) * Hkv * d * e * 2      # K, V in (valid entries)
             + B * Hq * Nq * d * e * 2        # Q in, O out
             + B * Hq * Nq * 4                # LSE out

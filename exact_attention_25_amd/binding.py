@@ -31,6 +31,10 @@ class AttnParams(ctypes.Structure):
         ("mask", ctypes.c_void_p),
         ("mask_sb", ctypes.c_int64), ("mask_sh", ctypes.c_int64), ("mask_sq", ctypes.c_int64),
         ("kv_lens", ctypes.c_void_p),
+        ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+        ("grid_cols", ctypes.c_int32), ("nbr_rows", ctypes.c_int32), ("nbr_cols", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
     ]
 
 
@@ -77,7 +81,11 @@ def attn_status_string(status: int) -> str:
 
 
 def make_params(B, Hq, Hkv, Nq, Nk, d, dtype=ATTN_BF16, layout=ATTN_BHND, scale=None,
-                causal=False, mask_ptr=None, mask_strides=(0, 0, 0), kv_lens_ptr=None) -> AttnParams:
+                causal=False, mask_ptr=None, mask_strides=(0, 0, 0), kv_lens_ptr=None,
+                window_size=(-1, -1), grid=None, softcap=0.0) -> AttnParams:
+    """attn_params for the C calls.  window_size = (left, right) as in
+    flash_attn_func (-1 = open side); grid = (cols, nbr_rows, nbr_cols) or
+    None; softcap 0 = off."""
     p = AttnParams()
     p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = B, Hq, Hkv, Nq, Nk, d
     p.dtype, p.layout = dtype, layout
@@ -86,6 +94,12 @@ def make_params(B, Hq, Hkv, Nq, Nk, d, dtype=ATTN_BF16, layout=ATTN_BHND, scale=
     p.mask = mask_ptr
     p.mask_sb, p.mask_sh, p.mask_sq = (int(x) for x in mask_strides)
     p.kv_lens = kv_lens_ptr
+    wl, wr = (int(x) for x in window_size)
+    p.window = 1 if (wl >= 0 or wr >= 0) else 0
+    p.window_left, p.window_right = wl, wr
+    if grid is not None:
+        p.grid_cols, p.nbr_rows, p.nbr_cols = (int(x) for x in grid)
+    p.softcap = float(softcap or 0.0)
     return p
 
 
@@ -141,12 +155,15 @@ def _stream_ptr(device):
 
 
 def attn_fwd(q, k, v, *, layout="bhnd", causal=False, scale=None, attn_mask=None,
-             kv_lens=None, out=None, lse=None):
+             kv_lens=None, window_size=(-1, -1), grid=None, softcap=0.0, out=None, lse=None):
     """Forward attention.  Returns (o, lse).
 
     q: [B,Hq,Nq,d] ("bhnd") or [B,Nq,Hq,d] ("bnhd"); k, v likewise with Hkv
     heads.  attn_mask: optional float32 tensor broadcastable to [B,Hq,Nq,Nk]
     (additive, logit units).  kv_lens: optional int32 [B] device tensor.
+    window_size: (left, right) sliding window, -1 = open side.  grid:
+    (cols, nbr_rows, nbr_cols) 2-D neighbourhood.  softcap: tanh soft cap of
+    the scaled logits (0 = off).
     """
     torch = _torch()
     lib = load()
@@ -159,7 +176,7 @@ def attn_fwd(q, k, v, *, layout="bhnd", causal=False, scale=None, attn_mask=None
         kv_lens = kv_lens.contiguous()
         lens_ptr = kv_lens.data_ptr()
     p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
-                    causal, mask_ptr, mstr, lens_ptr)
+                    causal, mask_ptr, mstr, lens_ptr, window_size, grid, softcap)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -186,10 +203,11 @@ def _mask_arg(attn_mask, B, Hq, Nq, Nk):
 
 
 def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, attn_mask=None,
-             kv_lens=None, grad_dtype="fp32", workspace=None):
+             kv_lens=None, window_size=(-1, -1), grid=None, softcap=0.0, grad_dtype="fp32",
+             workspace=None):
     """Backward attention from the forward's (o, lse).  Returns (dq, dk, dv).
 
-    attn_mask: the same optional additive float32 mask the forward took.
+    attn_mask, window_size, grid, softcap: the same ones the forward took.
     """
     torch = _torch()
     lib = load()
@@ -204,7 +222,7 @@ def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, 
         kv_lens = kv_lens.contiguous()
         lens_ptr = kv_lens.data_ptr()
     p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
-                    causal, mask_ptr, mstr, lens_ptr)
+                    causal, mask_ptr, mstr, lens_ptr, window_size, grid, softcap)
     gcode = ATTN_FP32 if grad_dtype == "fp32" else _dtype_code(q.dtype)
     gdt = torch.float32 if gcode == ATTN_FP32 else q.dtype
     dq = torch.empty(q.shape, dtype=gdt, device=q.device)
@@ -223,12 +241,14 @@ def attn_bwd(q, k, v, o, lse, dout, *, layout="bhnd", causal=False, scale=None, 
 
 
 def attn_decode(q, k, v, *, layout="bhnd", causal=False, scale=None, kv_lens=None,
-                workspace=None, out=None, lse=None):
+                window_size=(-1, -1), softcap=0.0, workspace=None, out=None, lse=None):
     """Split-KV decode: Nq new queries against the k/v cache.  Returns (o, lse).
 
     q: [B,Hq,Nq,d] ("bhnd") or [B,Nq,Hq,d] ("bnhd"); k, v: the cache with Hkv
     heads and Nk entries.  kv_lens: optional int32 [B] device tensor of valid
-    cache entries.  causal: query i sees keys j <= L - Nq + i.
+    cache entries.  Query i sits at position p = L - Nq + i: causal means
+    keys j <= p, window_size = (left, right) keys p - left .. p + right.
+    softcap: tanh soft cap of the scaled logits (0 = off).
     """
     torch = _torch()
     lib = load()
@@ -240,7 +260,7 @@ def attn_decode(q, k, v, *, layout="bhnd", causal=False, scale=None, kv_lens=Non
         kv_lens = kv_lens.contiguous()
         lens_ptr = kv_lens.data_ptr()
     p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
-                    causal, None, (0, 0, 0), lens_ptr)
+                    causal, None, (0, 0, 0), lens_ptr, window_size, None, softcap)
     need = attn_decode_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -25,6 +25,60 @@ float resolve_scale(const attn_params* p) {
   return s;
 }
 
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr int64_t kLocalMaxPositions = int64_t(1) << 29;   // Nq + Nk bound of local calls
+
+bool has_window(const attn_params* p) {
+  return p->window != 0 && (p->window_left >= 0 || p->window_right >= 0);
+}
+// window or grid: the local kernels
+bool is_local(const attn_params* p) { return has_window(p) || p->grid_cols > 0; }
+
+// Checks of the local fields shared by every entry point.
+attn_status validate_local(const attn_params* p) {
+  if (p->grid_cols < 0) return ATTN_EINVAL;
+  if (p->grid_cols > 0 && (p->nbr_rows < 1 || p->nbr_cols < 1)) return ATTN_EINVAL;
+  if (!(p->softcap >= 0.0f) || !isfinite(p->softcap)) return ATTN_EINVAL;
+  if (p->softcap > 0.0f && !isfinite(2.0f * resolve_scale(p) * kLog2eF / p->softcap))
+    return ATTN_EINVAL;
+  if ((has_window(p) || p->grid_cols > 0) && (int64_t)p->Nq + p->Nk >= kLocalMaxPositions)
+    return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+// Window and grid in kernel form: an open side becomes Nq + Nk (beyond every
+// position), causal caps the right side at 0, and the grid's column count
+// and row radius are clamped to values that leave the relation unchanged
+// but keep the kernels' index arithmetic inside int32.
+attn::LocalVis local_vis(const attn_params* p) {
+  const int32_t open = p->Nq + p->Nk;
+  attn::LocalVis L = {};
+  L.win_l = open;
+  L.win_r = open;
+  if (p->window) {
+    if (p->window_left >= 0) L.win_l = p->window_left < open ? p->window_left : open;
+    if (p->window_right >= 0) L.win_r = p->window_right < open ? p->window_right : open;
+  }
+  if (p->causal && L.win_r > 0) L.win_r = 0;
+  if (p->grid_cols > 0) {
+    // positions are < open, so with cols >= open every position is in row 0
+    // and its column is the position itself, as with the caller's value
+    L.cols = p->grid_cols < open ? p->grid_cols : open;
+    const int32_t rows = open / L.cols + 2;   // exceeds any row difference
+    L.nbr_r = p->nbr_rows < rows ? p->nbr_rows : rows;
+    L.nbr_c = p->nbr_cols < L.cols ? p->nbr_cols : L.cols;
+  }
+  return L;
+}
+
+void softcap_consts(const attn_params* p, float* a, float* c2) {
+  *a = *c2 = 0.0f;
+  if (p->softcap > 0.0f) {
+    *a = p->softcap * kLog2eF;
+    *c2 = 2.0f * resolve_scale(p) * kLog2eF / p->softcap;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -37,8 +91,12 @@ attn_status attn_validate(const attn_params* p, int for_backward) {
   if (p->dtype != ATTN_FP32 && p->dtype != ATTN_FP16 && p->dtype != ATTN_BF16) return ATTN_EINVAL;
   if (p->layout != ATTN_BHND && p->layout != ATTN_BNHD) return ATTN_EINVAL;
   if (p->causal && p->Nq != p->Nk) return ATTN_EINVAL;
+  if (is_local(p) && p->Nq != p->Nk) return ATTN_EINVAL;
   if (p->mask && (p->mask_sb < 0 || p->mask_sh < 0 || p->mask_sq < 0)) return ATTN_EINVAL;
+  const attn_status sl = validate_local(p);
+  if (sl != ATTN_OK) return sl;
   if (p->d < 8 || p->d > 128 || p->d % 8 != 0) return ATTN_EUNSUPPORTED;
+  if (for_backward && (is_local(p) || p->softcap > 0.0f)) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -71,14 +129,21 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.m_sb = p->mask_sb; a.m_sh = p->mask_sh; a.m_sq = p->mask_sq;
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.d = p->d;
   a.group = p->Hq / p->Hkv;
-  a.c = resolve_scale(p) * 1.4426950408889634f;
+  a.c = resolve_scale(p) * kLog2eF;
+  a.loc = local_vis(p);
+  softcap_consts(p, &a.cap_a, &a.cap_c2);
+  attn::FwdMode m;
+  m.local = is_local(p);
+  m.causal = p->causal != 0 && !m.local;   // folded into the window when local
+  m.mask = p->mask != nullptr;
+  m.softcap = p->softcap > 0.0f;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->dtype == ATTN_FP32)
-    e = attn::launch_fwd32(a, p->causal != 0, p->mask != nullptr, s);
+    e = attn::launch_fwd32(a, m, s);
   else
-    e = attn::launch_fwd16(a, p->dtype == ATTN_BF16, p->causal != 0, p->mask != nullptr, s);
+    e = attn::launch_fwd16(a, p->dtype == ATTN_BF16, m, s);
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -168,7 +233,7 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.d = p->d;
   a.group = p->Hq / p->Hkv;
   a.scale = resolve_scale(p);
-  a.c = a.scale * 1.4426950408889634f;
+  a.c = a.scale * kLog2eF;
   a.grad_f32 = grad_dtype == ATTN_FP32 ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = p->dtype == ATTN_FP32
@@ -181,16 +246,31 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
 
 namespace {
 
-// Validation of a decode call: attn_validate's rules, except that causal
-// (bottom-right aligned) does not need Nq == Nk; 16-bit dtypes, no mask.
+// Validation of a decode call: attn_validate's rules, except that causal and
+// the window (bottom-right aligned) do not need Nq == Nk; 16-bit dtypes, no
+// mask, no grid.
 attn_status validate_decode(const attn_params* p) {
   if (!p) return ATTN_EINVAL;
   attn_params c = *p;
   c.causal = 0;
-  const attn_status st = attn_validate(&c, 0);
+  c.window = 0;
+  const int grid = c.grid_cols;
+  c.grid_cols = 0;
+  attn_status st = attn_validate(&c, 0);
   if (st != ATTN_OK) return st;
-  if (p->dtype == ATTN_FP32 || p->mask) return ATTN_EUNSUPPORTED;
+  if (grid < 0) return ATTN_EINVAL;
+  // positions and window bounds stay far inside int32 (see local_vis)
+  if ((int64_t)p->Nq + p->Nk >= kLocalMaxPositions) return ATTN_EUNSUPPORTED;
+  if (p->dtype == ATTN_FP32 || p->mask || grid > 0) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
+}
+
+// Keys a decode call may read per batch: with a bounded left window only the
+// last Nq + window_left keys of each batch's L are visible to any query.
+int decode_span(const attn_params* p) {
+  if (has_window(p) && p->window_left >= 0 && (int64_t)p->Nq + p->window_left < p->Nk)
+    return p->Nq + p->window_left;
+  return p->Nk;
 }
 
 struct DecodeWorkspace {
@@ -201,7 +281,7 @@ struct DecodeWorkspace {
 DecodeWorkspace decode_workspace(const attn_params* p) {
   DecodeWorkspace w;
   const int rows = (p->Hq / p->Hkv) * p->Nq;
-  attn::decode_split(p->B, p->Hkv, rows, p->Nk, &w.split_keys, &w.n_splits);
+  attn::decode_split(p->B, p->Hkv, rows, decode_span(p), &w.split_keys, &w.n_splits);
   const size_t nrow = (size_t)p->B * p->Hq * p->Nq;
   w.part_o = align256((size_t)w.n_splits * nrow * p->d * sizeof(float));
   w.total = w.part_o + align256((size_t)w.n_splits * nrow * sizeof(float));
@@ -250,8 +330,16 @@ attn_status attn_decode(const attn_params* p, const void* q, const void* k, cons
   a.split_keys = ws.split_keys;
   a.n_splits = ws.n_splits;
   a.causal = p->causal ? 1 : 0;
-  a.c = resolve_scale(p) * 1.4426950408889634f;
-  const hipError_t e = attn::launch_decode(a, p->dtype == ATTN_BF16,
+  a.c = resolve_scale(p) * kLog2eF;
+  {
+    attn_params c = *p;
+    c.grid_cols = 0;
+    const attn::LocalVis L = local_vis(&c);   // open sides Nq + Nk, causal folded in
+    a.win_l = L.win_l;
+    a.win_r = L.win_r;
+  }
+  softcap_consts(p, &a.cap_a, &a.cap_c2);
+  const hipError_t e = attn::launch_decode(a, p->dtype == ATTN_BF16, p->softcap > 0.0f,
                                            reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }

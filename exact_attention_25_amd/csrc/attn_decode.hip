@@ -15,8 +15,15 @@
 // loads is all the synchronisation there is), computes S^T = K Q^T and
 // O^T += V^T P^T on MFMA exactly as the forward kernel does, and writes
 // the normalised partial O (fp32) and its LSE to the workspace.
+//
+// Query i of a batch with L valid keys sits at position p = L - Nq + i and
+// sees keys p - win_l .. p + win_r (causal and the sliding window, see
+// local_mask.h).  The splits tile only the keys some query can see, from
+// max(0, L - Nq - win_l) on, so a bounded window reads just its last keys.
+// SOFTCAP applies the tanh soft cap to the scaled logits.
 #include "attn_kernels.h"
 #include "device_common.h"
+#include "local_mask.h"
 
 namespace attn {
 
@@ -29,7 +36,7 @@ __host__ __device__ constexpr int vm_wait(int n) {
 // ... that waits for all LDS operations only (vmcnt and expcnt at their maxima)
 constexpr int kLdsOnly = 0xC07F;
 
-template <class E, int D>
+template <class E, int D, bool SOFTCAP>
 struct DecodeSplit {
   static constexpr int BC = 32;                 // keys per tile
   static constexpr int CPR = D / 8;
@@ -46,13 +53,14 @@ struct DecodeSplit {
 
   struct State {
     int hl, l32;
-    int row_lim;                // keys >= row_lim are excluded for this lane's row
+    int row_lo, row_lim;        // this lane's row sees keys row_lo .. row_lim - 1
     const char* kp;
     const char* vp;
     int64_t tile_bytes, k_end;
     uint32_t koff[K_INS], voff[V_INS];
     int kbase, vbase;
     float c;
+    float cap_a, cap_c2;        // soft cap constants (SOFTCAP)
     V8 qf[KS];
     f32x16 acc[DT];
     float m, l;
@@ -92,7 +100,8 @@ struct DecodeSplit {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
-      s[r] = key < st.row_lim ? s[r] * st.c : -INFINITY;
+      const float t = SOFTCAP ? softcap_log2(s[r], st.cap_a, st.cap_c2) : s[r] * st.c;
+      s[r] = (key >= st.row_lo && key < st.row_lim) ? t : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
     mx = max_with_other_half(mx);
@@ -155,13 +164,18 @@ struct DecodeSplit {
 
     int kv_limit = a.Nk;
     if (a.kv_lens) kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
-    st.row_lim = a.causal ? min(kv_limit, kv_limit - a.Nq + qi + 1) : kv_limit;
-    if (!valid) st.row_lim = 0;
-    const int key_lo = sp * a.split_keys;
+    const int pos = kv_limit - a.Nq + qi;   // this row's position (may be < 0)
+    st.row_lo = max(pos - a.win_l, 0);
+    st.row_lim = min(kv_limit, pos + a.win_r + 1);
+    if (!valid) st.row_lo = st.row_lim = 0;
+    // the splits start at the first key visible to the batch's first query
+    const int key_lo = max(kv_limit - a.Nq - a.win_l, 0) + sp * a.split_keys;
     const int key_hi = min(key_lo + a.split_keys, kv_limit);
     const int n_tiles = key_hi > key_lo ? (key_hi - key_lo + BC - 1) / BC : 0;
 
     st.c = a.c;
+    st.cap_a = a.cap_a;
+    st.cap_c2 = a.cap_c2;
     {
       const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh + (int64_t)qi * a.q_sn;
 #pragma unroll
@@ -233,9 +247,9 @@ struct DecodeSplit {
   }
 };
 
-template <class E, int D>
+template <class E, int D, bool SOFTCAP>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  using K = DecodeSplit<E, D>;
+  using K = DecodeSplit<E, D, SOFTCAP>;
   __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
@@ -345,12 +359,14 @@ void decode_split(int B, int Hkv, int rows, int Nk, int* split_keys, int* n_spli
   *n_splits = Nk > 0 ? (int)((Nk + sk - 1) / sk) : 1;
 }
 
-template <class E>
+template <class E, bool SOFTCAP>
 static hipError_t launch_decode_e(const DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((long)a.B * a.Hkv * a.n_rb * a.n_splits);
   if (grid > 0) {
-    if (a.d > 64) hipLaunchKernelGGL((decode_split_kernel<E, 128>), dim3(grid), dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((decode_split_kernel<E, 64>), dim3(grid), dim3(64), 0, st, a);
+    if (a.d > 64)
+      hipLaunchKernelGGL((decode_split_kernel<E, 128, SOFTCAP>), dim3(grid), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<E, 64, SOFTCAP>), dim3(grid), dim3(64), 0, st, a);
   }
   const long nrow = (long)a.B * a.Hq * a.Nq;
   if (nrow > 0)
@@ -358,8 +374,9 @@ static hipError_t launch_decode_e(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, hipStream_t st) {
-  return is_bf16 ? launch_decode_e<BF16>(a, st) : launch_decode_e<FP16>(a, st);
+hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, bool softcap, hipStream_t st) {
+  if (softcap) return is_bf16 ? launch_decode_e<BF16, true>(a, st) : launch_decode_e<FP16, true>(a, st);
+  return is_bf16 ? launch_decode_e<BF16, false>(a, st) : launch_decode_e<FP16, false>(a, st);
 }
 
 }  // namespace attn

@@ -1,7 +1,8 @@
 // Forward attention: kernel instances and dispatch.  Calls without a causal
 // or additive mask and with at least 8 key tiles take the software-pipelined
 // kernel (attn_fwd_pipe_kernel.h); the others take FwdKernel
-// (attn_fwd_kernel.h).  Both compute the same values.
+// (attn_fwd_kernel.h).  Both compute the same values.  Local and
+// soft-capped calls go to attn_fwd_local.hip.
 #include "attn_fwd_kernel.h"
 #include "attn_fwd_pipe_kernel.h"
 
@@ -40,8 +41,10 @@ static hipError_t launch_fwd_e(const FwdArgs& a, bool causal, bool mask, hipStre
   return launch_fwd_t<E, 64, 8, 64>(a, causal, mask, st);
 }
 
-hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, bool causal, bool mask, hipStream_t st) {
-  return is_bf16 ? launch_fwd_e<BF16>(a, causal, mask, st) : launch_fwd_e<FP16>(a, causal, mask, st);
+hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st) {
+  if (m.local || m.softcap) return launch_fwd16_local(a, is_bf16, m, st);
+  return is_bf16 ? launch_fwd_e<BF16>(a, m.causal, m.mask, st)
+                 : launch_fwd_e<FP16>(a, m.causal, m.mask, st);
 }
 
 }  // namespace attn

@@ -6,15 +6,23 @@
 // One work-group of 4 waves per (batch, q-head, 128 query rows); each wave
 // owns 32 rows.  K/V tiles of 32 keys go through LDS (row stride D+1 floats,
 // so a column read by 32 lanes hits 32 different banks).
+//
+// LOCAL / SOFTCAP as in the 16-bit FwdKernel: only the key tiles that may be
+// visible to the work-group's rows are loaded, a wave skips tiles without a
+// visible key for any of its lanes, and elements are masked through the
+// visibility bits of local_mask.h; the soft cap transforms S right after
+// QK^T.
 #include "attn_kernels.h"
 #include "device_common.h"
+#include "local_mask.h"
 
 namespace attn {
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool LOCAL, bool SOFTCAP>
 __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
   constexpr int BC = 32, NW = 4, ROWS = NW * 32, DT = D / 32, KS = D / 2, LD = D + 1;
   constexpr float TH = 8.0f;
+  constexpr bool PRE = MASK || SOFTCAP;   // S already in log2 units
   __shared__ float ks_[BC * LD];
   __shared__ float vs_[BC * LD];
 
@@ -36,7 +44,22 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
   if (a.kv_lens) kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
   int kv_end = kv_limit;
   if (CAUSAL) kv_end = min(kv_end, min(q_blk0 + ROWS, a.Nq));
-  const int n_tiles = (kv_end + BC - 1) / BC;
+  int t_begin = 0, t_end = (kv_end + BC - 1) / BC;
+  int w_lo = 0, w_hi = t_end;   // this wave's tiles
+  LocalVis::Row lrow{};
+  if constexpr (LOCAL) {
+    int lo, hi;
+    a.loc.key_range(q_blk0, min(q_blk0 + ROWS, a.Nq) - 1, kv_limit, lo, hi);
+    t_begin = lo / BC;
+    t_end = hi >= lo ? hi / BC + 1 : t_begin;
+    w_lo = w_hi = 0;
+    if (q_w0 < a.Nq) {
+      a.loc.key_range(q_w0, min(q_w0 + 31, a.Nq - 1), kv_limit, lo, hi);
+      w_lo = lo / BC;
+      w_hi = hi >= lo ? hi / BC + 1 : w_lo;
+    }
+    lrow = a.loc.row(min(qrow, a.Nq - 1));
+  }
 
   const float* qp = (const float*)a.q + b * a.q_sb + h * a.q_sh;
   const float* kp = (const float*)a.k + b * a.k_sb + g * a.k_sh;
@@ -56,7 +79,7 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = t_begin; j < t_end; ++j) {
     const int j0 = j * BC;
     __syncthreads();
     for (int idx = threadIdx.x; idx < BC * D; idx += NW * 64) {
@@ -66,34 +89,50 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
       vs_[r * LD + c] = c < a.d ? vp[grow * a.v_sn + c] : 0.f;
     }
     __syncthreads();
+    uint32_t bits = 0;   // LOCAL: bit i set iff key j0 + i is visible to this lane's row
+    if constexpr (LOCAL) {
+      if (j < w_lo || j >= w_hi) continue;
+      bits = (uint32_t)a.loc.bits(lrow, j0, kv_limit);
+      if (!__builtin_amdgcn_ballot_w64(bits != 0)) continue;
+    }
 
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks_[l32 * LD + 2 * ks + hl], qf[ks], s, 0, 0, 0);
 
+    if constexpr (SOFTCAP) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = softcap_log2(s[r], a.cap_a, a.cap_c2);
+    }
     if constexpr (MASK) {
       const int mrow = min(qrow, a.Nq - 1);
       const float* mp = a.mask + b * a.m_sb + h * a.m_sh + (int64_t)mrow * a.m_sq;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + (r >> 2) * 8 + hl * 4 + (r & 3);
-        s[r] = s[r] * a.c + mp[min(key, a.Nk - 1)] * kLog2e;
+        s[r] = (SOFTCAP ? s[r] : s[r] * a.c) + mp[min(key, a.Nk - 1)] * kLog2e;
       }
     }
-    const bool edge = (j0 + BC > kv_limit) || (CAUSAL && j0 + BC - 1 > q_w0);
-    if (edge) {
+    if constexpr (LOCAL) {
+      const uint32_t w = bits >> (hl * 4);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + (r >> 2) * 8 + hl * 4 + (r & 3);
-        if (key >= kv_limit || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) s[r] = keep_if_bit(s[r], w, (r >> 2) * 8 + (r & 3));
+    } else {
+      const bool edge = (j0 + BC > kv_limit) || (CAUSAL && j0 + BC - 1 > q_w0);
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if (key >= kv_limit || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+        }
       }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = max_with_other_half(mx);
-    const float cand = MASK ? mx : mx * a.c;
+    const float cand = PRE ? mx : mx * a.c;
     if (__builtin_amdgcn_ballot_w64(cand > m_run + TH)) {
       const float m_new = fmaxf(m_run, cand);
       const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
@@ -107,7 +146,7 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
     const float mref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float t = MASK ? (s[r] - mref) : __builtin_fmaf(s[r], a.c, -mref);
+      const float t = PRE ? (s[r] - mref) : __builtin_fmaf(s[r], a.c, -mref);
       s[r] = fast_exp2(t);
       l_run += s[r];
     }
@@ -143,25 +182,39 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
   }
 }
 
-template <int D>
-static hipError_t launch32_d(const FwdArgs& a, bool causal, bool mask, hipStream_t st) {
+template <int D, bool MASK, bool LOCAL, bool SOFTCAP>
+static void launch32_c(const FwdArgs& a, bool causal, hipStream_t st) {
   dim3 grid(a.total_blocks), block(256);
-  if (causal) {
-    if (mask) hipLaunchKernelGGL((fwd32_kernel<D, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd32_kernel<D, true, false>), grid, block, 0, st, a);
-  } else {
-    if (mask) hipLaunchKernelGGL((fwd32_kernel<D, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd32_kernel<D, false, false>), grid, block, 0, st, a);
-  }
-  return hipGetLastError();
+  if (causal && !LOCAL)
+    hipLaunchKernelGGL((fwd32_kernel<D, !LOCAL, MASK, LOCAL, SOFTCAP>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd32_kernel<D, false, MASK, LOCAL, SOFTCAP>), grid, block, 0, st, a);
 }
 
-hipError_t launch_fwd32(const FwdArgs& a0, bool causal, bool mask, hipStream_t st) {
+template <int D, bool MASK>
+static void launch32_m(const FwdArgs& a, FwdMode m, hipStream_t st) {
+  if (m.local) {
+    if (m.softcap) launch32_c<D, MASK, true, true>(a, false, st);
+    else launch32_c<D, MASK, true, false>(a, false, st);
+  } else {
+    if (m.softcap) launch32_c<D, MASK, false, true>(a, m.causal, st);
+    else launch32_c<D, MASK, false, false>(a, m.causal, st);
+  }
+}
+
+template <int D>
+static void launch32_d(const FwdArgs& a, FwdMode m, hipStream_t st) {
+  if (m.mask) launch32_m<D, true>(a, m, st);
+  else launch32_m<D, false>(a, m, st);
+}
+
+hipError_t launch_fwd32(const FwdArgs& a0, FwdMode m, hipStream_t st) {
   FwdArgs a = a0;
   a.nqb = (a.Nq + 127) / 128;
   a.total_blocks = a.B * a.Hq * a.nqb;
-  if (a.d > 64) return launch32_d<128>(a, causal, mask, st);
-  return launch32_d<64>(a, causal, mask, st);
+  if (a.d > 64) launch32_d<128>(a, m, st);
+  else launch32_d<64>(a, m, st);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -29,17 +29,33 @@
 //                        registers (keys are matched slot by slot).
 // Epilogue: O /= l (one reciprocal per row), round to the output type,
 // LSE = ln2 * (m + log2 l).
+//
+// Local attention (LOCAL: sliding window and/or 2-D neighbourhood, with
+// causal masking folded into the window, see local_mask.h): the work-group
+// loads only the key tiles that may be visible to one of its rows, and each
+// wave computes only the tiles inside its own rows' key range that hold a
+// visible key for at least one of its lanes; the elements of those tiles are
+// masked through a 64-bit visibility word per lane (skipped when every key
+// of the tile is visible to every row).  SOFTCAP replaces each scaled logit
+// by cap * tanh(logit / cap) right after QK^T.
 #pragma once
 
 #include "attn_kernels.h"
 #include "device_common.h"
+#include "local_mask.h"
 
 namespace attn {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p stays <= 256
 
-template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
+template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK, bool LOCAL = false,
+          bool SOFTCAP = false>
 struct FwdKernel {
+  static_assert(!(LOCAL && CAUSAL), "causal masking is part of the window under LOCAL");
+  static_assert(!LOCAL || BC == 64, "LOCAL masks a tile through one 64-bit word");
+  // scores leave the QK^T step already in log2 units (otherwise the scale
+  // is folded into the exponent)
+  static constexpr bool PRE = MASK || SOFTCAP;
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   // LDS row pitches in 16-byte slots.  K rows get one pad slot: the 16 rows
   // that one read instruction touches at a time (same chunk) then fall on 16
@@ -71,6 +87,8 @@ struct FwdKernel {
     int q_w0;                   // first query row of this wave
     int kv_limit;               // keys >= kv_limit are excluded
     int n_act;                  // tiles this wave has to visit (causal)
+    int t_lo, t_hi;             // LOCAL: this wave's tiles [t_lo, t_hi)
+    LocalVis::Row lrow;         // LOCAL: this lane's query position
     const char* kp;             // K / V of this (batch, kv-head), key 0
     const char* vp;
     int64_t k_tile, v_tile;     // bytes between consecutive tiles
@@ -115,9 +133,10 @@ struct FwdKernel {
     }
   }
 
-  // One KV tile: S^T, masking, online softmax, PV.
+  // One KV tile: S^T, masking, online softmax, PV.  bits (LOCAL): bit i set
+  // iff key j0 + i is visible to this lane's row.
   static __device__ __forceinline__ void tile(const FwdArgs& a, State& st, const char* kbuf,
-                                              const char* vbuf, int j0) {
+                                              const char* vbuf, int j0, uint64_t bits) {
     // S^T = K_j Q^T
     f32x16 s[KB];
 #pragma unroll
@@ -132,6 +151,12 @@ struct FwdKernel {
     }
 
     const int qrow = st.q_w0 + st.l32;
+    if constexpr (SOFTCAP) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[k][r] = softcap_log2(s[k][r], a.cap_a, a.cap_c2);
+    }
     if constexpr (MASK) {
       const int mrow = min(qrow, a.Nq - 1);
       const float* mp = a.mask + st.b * a.m_sb + st.h * a.m_sh + (int64_t)mrow * a.m_sq;
@@ -140,18 +165,30 @@ struct FwdKernel {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + k * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
-          s[k][r] = s[k][r] * st.c + mp[min(key, a.Nk - 1)] * kLog2e;
+          s[k][r] = (SOFTCAP ? s[k][r] : s[k][r] * st.c) + mp[min(key, a.Nk - 1)] * kLog2e;
         }
     }
-    const bool edge = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
-    if (edge) {
+    if constexpr (LOCAL) {
+      // lane half hl holds keys k*32 + (r/4)*8 + 4 hl + r%4 of the tile
+      if (__builtin_amdgcn_ballot_w64(bits != ~0ull)) {
 #pragma unroll
-      for (int k = 0; k < KB; ++k)
+        for (int k = 0; k < KB; ++k) {
+          const uint32_t w = (uint32_t)(bits >> (k * 32 + st.hl * 4));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + k * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
-          if (key >= st.kv_limit || (CAUSAL && key > qrow)) s[k][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) s[k][r] = keep_if_bit(s[k][r], w, (r >> 2) * 8 + (r & 3));
         }
+      }
+    } else {
+      const bool edge = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
+      if (edge) {
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + k * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
+            if (key >= st.kv_limit || (CAUSAL && key > qrow)) s[k][r] = -INFINITY;
+          }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -159,7 +196,7 @@ struct FwdKernel {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[k][r]);
     mx = max_with_other_half(mx);
-    const float cand = MASK ? mx : mx * st.c;
+    const float cand = PRE ? mx : mx * st.c;
     if (__builtin_amdgcn_ballot_w64(cand > st.m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(st.m_run, cand);
       if (m_new > st.m_run) {
@@ -180,8 +217,8 @@ struct FwdKernel {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float x0 = s[k][r0 + 2 * q], x1 = s[k][r0 + 2 * q + 1];
-        x0 = fast_exp2(MASK ? x0 - mref : __builtin_fmaf(x0, st.c, -mref));
-        x1 = fast_exp2(MASK ? x1 - mref : __builtin_fmaf(x1, st.c, -mref));
+        x0 = fast_exp2(PRE ? x0 - mref : __builtin_fmaf(x0, st.c, -mref));
+        x1 = fast_exp2(PRE ? x1 - mref : __builtin_fmaf(x1, st.c, -mref));
         lsum += x0 + x1;
         pp[q] = E::cvt2(x0, x1);
       }
@@ -204,12 +241,19 @@ struct FwdKernel {
     }
   }
 
-  static __device__ __forceinline__ void step(const FwdArgs& a, State& st, int j, int n_tiles,
+  static __device__ __forceinline__ void step(const FwdArgs& a, State& st, int j, int t_end,
                                               const char* kc, const char* vc, char* kn, char* vn) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile j has landed
     __syncthreads();
-    if (j + 1 < n_tiles) issue(st, (j + 1) * BC, kn, vn);
-    if (j < st.n_act) tile(a, st, kc, vc, j * BC);
+    if (j + 1 < t_end) issue(st, (j + 1) * BC, kn, vn);
+    if constexpr (LOCAL) {
+      if (j >= st.t_lo && j < st.t_hi) {
+        const uint64_t bits = a.loc.bits(st.lrow, j * BC, st.kv_limit);
+        if (__builtin_amdgcn_ballot_w64(bits != 0)) tile(a, st, kc, vc, j * BC, bits);
+      }
+    } else {
+      if (j < st.n_act) tile(a, st, kc, vc, j * BC, 0);
+    }
   }
 
   static __device__ __forceinline__ void run(const FwdArgs& a, char* k0, char* v0, char* k1,
@@ -277,11 +321,26 @@ struct FwdKernel {
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
-    if (n_tiles > 0) issue(st, 0, k0, v0);
-    for (int j = 0; j < n_tiles; j += 2) {
-      step(a, st, j, n_tiles, k0, v0, k1, v1);
-      if (j + 1 >= n_tiles) break;
-      step(a, st, j + 1, n_tiles, k1, v1, k0, v0);
+    // tiles [t_begin, t_end) pass through LDS
+    int t_begin = 0, t_end = n_tiles;
+    if constexpr (LOCAL) {
+      int lo, hi;
+      a.loc.key_range(q_blk0, min(q_blk0 + ROWS, a.Nq) - 1, st.kv_limit, lo, hi);
+      t_begin = lo / BC;
+      t_end = hi >= lo ? hi / BC + 1 : t_begin;
+      st.t_lo = st.t_hi = 0;
+      if (st.q_w0 < a.Nq) {
+        a.loc.key_range(st.q_w0, min(st.q_w0 + 31, a.Nq - 1), st.kv_limit, lo, hi);
+        st.t_lo = lo / BC;
+        st.t_hi = hi >= lo ? hi / BC + 1 : st.t_lo;
+      }
+      st.lrow = a.loc.row(min(st.q_w0 + st.l32, a.Nq - 1));
+    }
+    if (t_begin < t_end) issue(st, t_begin * BC, k0, v0);
+    for (int j = t_begin; j < t_end; j += 2) {
+      step(a, st, j, t_end, k0, v0, k1, v1);
+      if (j + 1 >= t_end) break;
+      step(a, st, j + 1, t_end, k1, v1, k0, v0);
     }
 
     // Epilogue.
@@ -310,10 +369,11 @@ struct FwdKernel {
   }
 };
 
-template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
+template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK, bool LOCAL = false,
+          bool SOFTCAP = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void fwd_kernel(FwdArgs a) {
-  using K = FwdKernel<E, D, NW, BC, CAUSAL, MASK>;
+  using K = FwdKernel<E, D, NW, BC, CAUSAL, MASK, LOCAL, SOFTCAP>;
   __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];

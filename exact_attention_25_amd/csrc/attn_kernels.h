@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "local_mask.h"
+
 namespace attn {
 
 // Kernel arguments of the forward pass.  Strides are in elements; d is the
@@ -26,6 +28,8 @@ struct FwdArgs {
   int32_t nqb;           // query blocks per head (set by the launcher)
   int32_t total_blocks;  // B * Hq * nqb (set by the launcher)
   float c;               // scale * log2(e)
+  LocalVis loc;          // window / grid (local launches only)
+  float cap_a, cap_c2;   // soft cap: cap * log2(e), 2 * scale * log2(e) / cap
 };
 
 // Kernel arguments of the backward pass (16-bit inputs).
@@ -87,18 +91,32 @@ struct DecodeArgs {
   int32_t n_splits;      // ceil(Nk / split_keys)
   int32_t causal;        // 1: query i sees keys j <= L - Nq + i (L = the batch's key count)
   float c;               // scale * log2(e)
+  // query i (position p = L - Nq + i) sees keys p - win_l .. p + win_r; an
+  // open side is Nq + Nk, and causal is folded in as win_r <= 0
+  int32_t win_l, win_r;
+  float cap_a, cap_c2;   // soft cap (see FwdArgs), used when soft-capped
 };
 
 // Split of the decode's keys, shared by the workspace sizing and the launch.
 void decode_split(int B, int Hkv, int rows, int Nk, int* split_keys, int* n_splits);
-hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, bool softcap, hipStream_t st);
 
 // Work split of the backward, shared by the workspace sizing and the launch.
 constexpr int kBwdKeysPerBlock = 128;   // keys per dK/dV work-group
 int bwd_kv_chunks(int B, int Hkv, int Nk, int group);
 
-hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, bool causal, bool mask, hipStream_t st);
-hipError_t launch_fwd32(const FwdArgs& a, bool causal, bool mask, hipStream_t st);
+// Variant switches of a forward launch.
+struct FwdMode {
+  bool causal;    // causal, outside local launches
+  bool mask;      // additive mask
+  bool local;     // window and/or grid in a.loc (causal folded into it)
+  bool softcap;   // soft cap (a.cap_a, a.cap_c2)
+};
+
+hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);
+// Local / soft-capped 16-bit launches (attn_fwd_local.hip).
+hipError_t launch_fwd16_local(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);
+hipError_t launch_fwd32(const FwdArgs& a, FwdMode m, hipStream_t st);
 hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, bool causal, hipStream_t st);
 // fp32 backward (attn_bwd32.hip): D from dO and O, then dQ and dK/dV on the fp32 MFMA.
 hipError_t launch_bwd32(const BwdArgs& a, bool causal, hipStream_t st);

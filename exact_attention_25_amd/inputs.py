@@ -14,8 +14,12 @@ The workloads stand in for the pages' cases (no dataset is used): a tiny fp32
 case; a ViT at 224x224 with 16x16 patches (196 tokens, 16 heads of 64); a
 Stable-Diffusion-1.5 UNet latent of 64x64 (4096 tokens, 8 heads of 40) with a
 77-token text cross-attention whose valid lengths vary per sample; the
-B8 H32 N4096 d128 benchmark shape; and a causal grouped-query decoder at 8192
-tokens with per-sequence valid lengths.
+B8 H32 N4096 d128 benchmark shape; a causal grouped-query decoder at 8192
+tokens with per-sequence valid lengths; decode steps against a 32K cache; and
+the FlexAttention cases of the PyTorch attention-options article (a ViT with
+3136 tokens under the tanh soft cap or the 2-D neighbourhood mask).  A
+workload may draw q and k with their own std (``qk_std``), so that the
+logits reach a soft cap while v keeps unit scale.
 """
 from __future__ import annotations
 
@@ -42,6 +46,11 @@ class Workload:
     causal: bool = False
     lens: tuple | None = None   # inclusive uniform range of valid key counts
     backward: bool = False
+    # local attention / soft cap of the call (see attn_params in include/attn.h)
+    window: tuple | None = None  # (left, right), -1 = open side
+    grid: tuple | None = None    # (cols, nbr_rows, nbr_cols)
+    softcap: float = 0.0
+    qk_std: float | None = None  # std of q and k when it differs from std (v, dO)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -61,6 +70,19 @@ WORKLOADS = {
         # valid lengths vary over the batch (served with attn_decode)
         Workload("decode_bf16_b8_hq32_kv8_q1_nk32768_d128", 8, 32, 8, 1, 32768, 128, "bf16", 6,
                  lens=(16384, 32768)),
+        # the FlexAttention examples of the PyTorch attention-options article:
+        # a ViT at 224x224 with 4x4 patches (56 x 56 = 3136 tokens, 12 heads of
+        # 64, batch 8), once with the tanh soft cap 30 (inputs scaled so that
+        # the logits reach the cap) and once with the neighbourhood mask (row
+        # and column differences < 5 on the 56 x 56 grid)
+        Workload("vit_softcap_bf16_b8_h12_n3136_d64", 8, 12, 12, 3136, 3136, 64, "bf16", 7,
+                 qk_std=2.5, softcap=30.0),
+        Workload("vit_nbr_bf16_b8_h12_n3136_d64", 8, 12, 12, 3136, 3136, 64, "bf16", 8,
+                 grid=(56, 5, 5)),
+        # a sliding-window decode step: one new token, window of 4096 keys
+        # behind it, against the same 32K cache
+        Workload("decode_window_bf16_b8_hq32_kv8_q1_nk32768_d128", 8, 32, 8, 1, 32768, 128,
+                 "bf16", 9, causal=True, lens=(16384, 32768), window=(4095, 0)),
     ]
 }
 
@@ -129,7 +151,8 @@ def make_inputs(w: Workload, with_do: bool | None = None) -> dict:
     if with_do or (with_do is None and w.backward):
         names.append("do")
     for t in names:
-        exact, raw = storage(draw(w.seed, t, shapes[t], w.std), w.dtype)
+        std = w.qk_std if (w.qk_std is not None and t in ("q", "k")) else w.std
+        exact, raw = storage(draw(w.seed, t, shapes[t], std), w.dtype)
         out[t] = exact
         out[t + "_raw"] = raw
     out["kv_lens"] = None if w.lens is None else draw_lens(w.seed, w.B, *w.lens)

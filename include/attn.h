@@ -19,9 +19,13 @@
  *     recomputing P in the backward: same page §3.3;
  *   - the call surfaces that fix the argument set: F.scaled_dot_product_attention
  *     (q, k, v in [B, H, N, d], attn_mask, is_causal) and
- *     flash_attn_func(q, k, v, softmax_scale, causal, deterministic) in
- *     [B, N, H, d] -- "如何在ChatGLM2-6B中集成Flash-Attention2？实测性能提升与
- *     显存优化" (jsqmd.com/news/348824) §3 steps 3 and 4.
+ *     flash_attn_func(q, k, v, softmax_scale, causal, window_size,
+ *     deterministic) in [B, N, H, d] -- "如何在ChatGLM2-6B中集成Flash-Attention2？
+ *     实测性能提升与显存优化" (jsqmd.com/news/348824) §3 steps 3 and 4;
+ *   - the tanh soft cap (score_mod) and the 2-D neighbourhood mask
+ *     (mask_mod / block_mask) of FlexAttention: the PyTorch
+ *     attention-options article (atyun.com/61003), sections
+ *     "Score Mod示例：使用Tanh进行软上限" and "Mask Mod示例：邻域屏蔽".
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
@@ -84,16 +88,38 @@ typedef struct {
   /* Optional [B] int32 valid key counts: keys j >= kv_lens[b] are excluded.
    * Values are clamped to [0, Nk].  NULL = all Nk keys are valid. */
   const int32_t* kv_lens;
+  /* Local attention and the soft cap; a zero-filled tail means none of them.
+   * Query row i sits at position p = i in attn_fwd / attn_bwd and at
+   * p = L - Nq + i in attn_decode (L = kv_lens[b] or Nk).
+   *   window != 0: sliding window (flash_attn_func's window_size =
+   *     (window_left, window_right)): key j is visible iff
+   *     p - window_left <= j <= p + window_right; a negative bound leaves its
+   *     side open.  Combines with causal (which then caps the right side).
+   *   grid_cols > 0: 2-D neighbourhood: position t is the cell
+   *     (t / grid_cols, t % grid_cols) of a row-major grid, and key j is
+   *     visible iff |row(p) - row(j)| < nbr_rows and
+   *     |col(p) - col(j)| < nbr_cols (both >= 1).  attn_fwd / attn_bwd only.
+   *   softcap > 0: the scaled logit s = scale * q.k becomes
+   *     softcap * tanh(s / softcap) before the additive mask.  0 = off.
+   * A key excluded by any rule is excluded (the rules intersect).  With a
+   * window or grid, attn_fwd / attn_bwd need Nq == Nk and Nq + Nk < 2^29;
+   * attn_decode always needs Nq + Nk < 2^29. */
+  int32_t window;
+  int32_t window_left, window_right;
+  int32_t grid_cols, nbr_rows, nbr_cols;
+  float softcap;
 } attn_params;
 
-/* Host-only check of *p (no GPU call).  for_backward != 0 also checks the
- * backward's extra constraints.  Returns ATTN_OK, ATTN_EINVAL (null p, shapes
- * out of range (B, Nq, Nk < 0; Hq, Hkv, d < 1), Hq % Hkv != 0, causal with
- * Nq != Nk, bad enum, negative mask stride) or ATTN_EUNSUPPORTED (d outside
- * [8, 128] or d % 8 != 0; for the backward also an additive mask or an fp32
- * dtype).  B == 0, Nq == 0 and Nk == 0 are
- * valid: the first two make a call a no-op, the last makes every row fully
- * masked. */
+/* Host-only check of *p (no GPU call) for attn_fwd (for_backward == 0) or
+ * attn_bwd (for_backward != 0).  Returns ATTN_OK, ATTN_EINVAL (null p,
+ * shapes out of range (B, Nq, Nk < 0; Hq, Hkv, d < 1), Hq % Hkv != 0, causal,
+ * window or grid with Nq != Nk, bad enum, negative mask stride, grid_cols < 0,
+ * grid_cols > 0 with nbr_rows or nbr_cols < 1, softcap negative or not
+ * finite, or so small that 2 * scale * log2(e) / softcap overflows) or
+ * ATTN_EUNSUPPORTED (d outside [8, 128] or d % 8 != 0; a window or grid with
+ * Nq + Nk >= 2^29; for the backward, a window, grid or soft cap).  B == 0,
+ * Nq == 0 and Nk == 0 are valid: the first two make a call a no-op, the last
+ * makes every row fully masked. */
 attn_status attn_validate(const attn_params* p, int for_backward);
 
 /* Forward pass.
@@ -152,8 +178,10 @@ size_t attn_decode_workspace_bytes(const attn_params* p);
  *   causal: the Nq queries are the last Nq positions of the sequence: query
  *      i sees keys j <= L - Nq + i, with L = kv_lens[b] (or Nk).  Unlike
  *      attn_fwd, Nq may differ from Nk.
- * 16-bit dtypes only and no additive mask (ATTN_EUNSUPPORTED otherwise);
- * other parameters as for attn_fwd.
+ *   window / softcap: as for attn_fwd, at position p = L - Nq + i; with a
+ *      bounded window_left only the last Nq + window_left keys are read.
+ * 16-bit dtypes only, no additive mask and no grid (ATTN_EUNSUPPORTED
+ * otherwise); Nq + Nk < 2^29; other parameters as for attn_fwd.
  *   workspace: device memory of at least attn_decode_workspace_bytes(p)
  *              bytes, 16-byte aligned; its contents on entry do not matter.
  * Deterministic: the splits are merged in a fixed order. */

@@ -34,8 +34,10 @@ def host(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed, std=1.0, lens=None, with_do=False):
-    w = inputs.Workload("case", B, Hq, Hkv, Nq, Nk, d, dtype, seed, std=std, lens=lens)
+def make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed, std=1.0, lens=None, with_do=False,
+              qk_std=None):
+    w = inputs.Workload("case", B, Hq, Hkv, Nq, Nk, d, dtype, seed, std=std, lens=lens,
+                        qk_std=qk_std)
     return w, inputs.make_inputs(w, with_do=with_do)
 
 

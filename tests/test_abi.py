@@ -28,11 +28,29 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
-def test_params_struct_matches_header_layout():
-    # int32 x6, two enums, float, int32, pointer, int64 x3, pointer
-    assert ctypes.sizeof(bd.AttnParams) == 80
-    assert bd.AttnParams.mask.offset == 40
-    assert bd.AttnParams.kv_lens.offset == 72
+def test_params_struct_matches_header_layout(tmp_path):
+    """ctypes' AttnParams has the size and field offsets a C compiler gives
+    attn_params from include/attn.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in bd.AttnParams._fields_]
+    prog = ['#include <stdio.h>', '#include <stddef.h>', '#include "attn.h"', 'int main(void) {',
+            '  printf("size %zu\\n", sizeof(attn_params));']
+    prog += [f'  printf("{f} %zu\\n", offsetof(attn_params, {f}));' for f in fields]
+    prog += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)],
+                   check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(bd.AttnParams)
+    for f in fields:
+        assert int(out[f]) == getattr(bd.AttnParams, f).offset, f
 
 
 def _p(**kw):
@@ -138,3 +156,41 @@ def test_decode_validation_and_errors():
     assert lib.attn_decode(ctypes.byref(p), *args, 16, need, None) == bd.ATTN_EALIGN
     bad = _p(d=44)
     assert lib.attn_decode(ctypes.byref(bad), *([16] * 5), 16, 1 << 30, None) == bd.ATTN_EUNSUPPORTED
+
+
+def test_local_and_softcap_validation():
+    ok, inv, uns = bd.ATTN_OK, bd.ATTN_EINVAL, bd.ATTN_EUNSUPPORTED
+    assert bd.attn_validate(_p(window_size=(16, 0))) == ok
+    assert bd.attn_validate(_p(window_size=(-1, -1), Nk=65)) == ok      # no window
+    assert bd.attn_validate(_p(window_size=(16, 0), Nk=65)) == inv      # needs Nq == Nk
+    assert bd.attn_validate(_p(grid=(8, 2, 2))) == ok
+    assert bd.attn_validate(_p(grid=(8, 2, 2), Nk=65)) == inv
+    assert bd.attn_validate(_p(grid=(8, 0, 2))) == inv
+    assert bd.attn_validate(_p(grid=(8, 2, 0))) == inv
+    p = _p()
+    p.grid_cols = -1
+    assert bd.attn_validate(p) == inv
+    assert bd.attn_validate(_p(softcap=30.0, Nk=65)) == ok             # soft cap alone: any Nk
+    assert bd.attn_validate(_p(softcap=-1.0)) == inv
+    assert bd.attn_validate(_p(softcap=float("nan"))) == inv
+    assert bd.attn_validate(_p(softcap=float("inf"))) == inv
+    assert bd.attn_validate(_p(softcap=1e-44)) == inv                  # 2 scale log2e / cap overflows
+    big = (1 << 28) + 10
+    assert bd.attn_validate(_p(Nq=big, Nk=big, window_size=(8, 8))) == uns
+    # the backward does not take them
+    assert bd.attn_validate(_p(window_size=(16, 0)), True) == uns
+    assert bd.attn_validate(_p(grid=(8, 2, 2)), True) == uns
+    assert bd.attn_validate(_p(softcap=5.0), True) == uns
+
+
+def test_decode_local_validation():
+    ws = bd.attn_decode_workspace_bytes
+    base = dict(B=2, Hq=8, Hkv=2, Nq=2, Nk=4096, d=128)
+    assert ws(bd.make_params(**base, window_size=(511, 0), causal=True)) > 0
+    assert ws(bd.make_params(**base, softcap=30.0)) > 0
+    assert ws(bd.make_params(**base, grid=(64, 2, 2))) == 0            # no grid in decode
+    assert ws(bd.make_params(**dict(base, Nk=(1 << 29)))) == 0         # position bound
+    # a bounded window shrinks the splits (and the workspace) to the window
+    full = ws(bd.make_params(**dict(base, Nk=65536), causal=True))
+    win = ws(bd.make_params(**dict(base, Nk=65536), causal=True, window_size=(1023, 0)))
+    assert 0 < win < full

@@ -1,0 +1,216 @@
+"""GPU parity of local attention and the soft cap against the fp64 oracle.
+
+Sliding window (flash_attn_func's window_size), 2-D neighbourhood (the
+FlexAttention mask_mod example) and the tanh soft cap (the score_mod example)
+in attn_fwd for all three dtypes, and the window and soft cap in attn_decode.
+The oracle takes the same options (oracle.attention_ref: window, grid,
+softcap, bottom_right for decode's positions), pinned in
+tests/test_oracle_local.py.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from exact_attention_25_amd import inputs
+from oracle import ref_fwd, ref_fwd_rows
+from tests.gpu_util import check_out, from_layout, host, make_case, to_device, to_layout
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, w, layout):
+    import torch
+    t = {n: to_device(to_layout(x[n + "_raw"], layout), w.dtype) for n in ("q", "k", "v")}
+    t["lens"] = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).cuda()
+    return t
+
+
+def _mask(B, Nq, Nk, seed):
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal((B, 1, Nq, Nk)).astype(np.float32)
+    m[rng.random((B, 1, Nq, Nk)) < 0.05] = -np.inf
+    return m
+
+
+FWD = [
+    # id, B, Hq, Hkv, N, d, dtype, layout, lens, qk_std (v has std 1), opts
+    ("bf16_window_64_0", 2, 4, 2, 1000, 128, "bf16", "bhnd", None, 1.0,
+     dict(window=(64, 0))),
+    ("fp16_window_100_37_lens_bnhd", 2, 4, 4, 777, 64, "fp16", "bnhd", (300, 777), 1.0,
+     dict(window=(100, 37))),
+    ("bf16_window_diagonal", 1, 2, 1, 300, 128, "bf16", "bhnd", None, 1.0,
+     dict(window=(0, 0))),
+    ("bf16_causal_window_300", 1, 4, 1, 2000, 64, "bf16", "bhnd", None, 1.0,
+     dict(window=(300, -1), causal=True)),
+    ("fp16_right_window_only_d40", 2, 2, 2, 513, 40, "fp16", "bhnd", None, 1.0,
+     dict(window=(-1, 5))),
+    ("bf16_grid_56x56_r5", 1, 2, 2, 3136, 64, "bf16", "bhnd", None, 1.0,
+     dict(grid=(56, 5, 5))),
+    ("fp16_grid_causal_mask", 2, 2, 1, 200, 64, "fp16", "bhnd", None, 1.0,
+     dict(grid=(7, 2, 3), causal=True, mask=True)),
+    ("bf16_grid_thin_cols", 1, 2, 2, 260, 128, "bf16", "bnhd", None, 1.0,
+     dict(grid=(1, 70, 1))),
+    ("bf16_softcap_2", 2, 4, 2, 1000, 64, "bf16", "bhnd", None, 2.0, dict(softcap=2.0)),
+    ("bf16_softcap_30_big_logits", 1, 4, 4, 1500, 128, "bf16", "bhnd", None, 2.5,
+     dict(softcap=30.0)),
+    ("fp16_softcap_causal_mask_lens", 2, 4, 2, 640, 128, "fp16", "bnhd", (100, 640), 2.0,
+     dict(softcap=5.0, causal=True, mask=True)),
+    ("bf16_all_options", 2, 4, 2, 700, 128, "bf16", "bhnd", (350, 700), 2.0,
+     dict(window=(200, 90), grid=(25, 4, 6), softcap=4.0, mask=True)),
+    ("fp32_window_softcap", 1, 2, 1, 300, 64, "fp32", "bhnd", None, 1.5,
+     dict(window=(40, 10), softcap=5.0)),
+    ("fp32_grid_causal", 1, 2, 2, 150, 128, "fp32", "bnhd", (90, 150), 1.0,
+     dict(grid=(12, 2, 3), causal=True)),
+    ("fp32_softcap_mask", 2, 2, 1, 200, 32, "fp32", "bhnd", None, 1.5,
+     dict(softcap=3.0, mask=True)),
+]
+
+
+def _fwd_case(case):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    name, B, Hq, Hkv, N, d, dtype, layout, lens, std, opts = case
+    opts = dict(opts)
+    seed = zlib.crc32(name.encode()) % 10000
+    w, x = make_case(B, Hq, Hkv, N, N, d, dtype, seed=seed, qk_std=std, lens=lens)
+    mask = _mask(B, N, N, seed) if opts.pop("mask", False) else None
+    causal = opts.pop("causal", False)
+    t = _dev(x, w, layout)
+    mt = None if mask is None else torch.from_numpy(mask).cuda()
+    o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], layout=layout, causal=causal, attn_mask=mt,
+                         kv_lens=t["lens"], window_size=opts.get("window", (-1, -1)),
+                         grid=opts.get("grid"), softcap=opts.get("softcap", 0.0))
+    torch.cuda.synchronize()
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], causal=causal, mask=mask,
+                           kv_lens=x["kv_lens"], **opts)
+    return from_layout(host(o), layout), lse, O_ref, L_ref, dtype
+
+
+@pytest.mark.parametrize("case", FWD, ids=[c[0] for c in FWD])
+def test_local_forward(gpu_lib, case):
+    _say(f"[local-fwd] {case[0]}")
+    o, lse, O_ref, L_ref, dtype = _fwd_case(case)
+    check_out(o, lse, O_ref, L_ref, dtype, case[0])
+
+
+def test_local_forward_rows_without_keys(gpu_lib):
+    """Rows that see no key: batch 0 has no valid key, and in batch 1 (150
+    valid keys) the window (10, 0) leaves rows 160.. without one: O = 0 and
+    LSE = -inf there, the rest as the oracle."""
+    import torch
+    from exact_attention_25_amd import binding as bd
+    _say("[local-fwd] empty rows")
+    w, x = make_case(2, 2, 2, 300, 300, 64, "bf16", seed=31, lens=(150, 150))
+    x["kv_lens"][0] = 0
+    t = _dev(x, w, "bhnd")
+    o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], kv_lens=t["lens"], window_size=(10, 0))
+    torch.cuda.synchronize()
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], window=(10, 0))
+    assert np.isneginf(L_ref[0]).all() and np.isneginf(L_ref[1, :, 160:]).all()
+    assert np.isfinite(L_ref[1, :, :160]).all()
+    check_out(host(o), lse, O_ref, L_ref, "bf16", "window empty rows")
+    assert np.all(host(o)[1, :, 160:] == 0)
+
+
+def test_local_forward_equals_plain_when_open(gpu_lib):
+    """A window wider than the sequence and a grid wider than the grid give
+    the same output as the plain kernel (up to rounding of the two paths)."""
+    import torch
+    from exact_attention_25_amd import binding as bd
+    _say("[local-fwd] open window equals plain")
+    w, x = make_case(1, 4, 2, 900, 900, 128, "bf16", seed=77)
+    t = _dev(x, w, "bhnd")
+    o0, l0 = bd.attn_fwd(t["q"], t["k"], t["v"])
+    o1, l1 = bd.attn_fwd(t["q"], t["k"], t["v"], window_size=(5000, 5000))
+    o2, l2 = bd.attn_fwd(t["q"], t["k"], t["v"], grid=(30, 40, 30))
+    torch.cuda.synchronize()
+    for o, l in ((o1, l1), (o2, l2)):
+        assert float((o.float() - o0.float()).abs().max()) <= 8e-3
+        assert float((l - l0).abs().max()) <= 1e-4
+
+
+DEC = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, layout, lens, qk_std, causal, window, softcap
+    ("bf16_window_decode_nq1", 2, 8, 2, 1, 5000, 128, "bf16", "bhnd", (1000, 5000), 1.0,
+     True, (700, 0), 0.0),
+    ("fp16_window_decode_nq4_softcap", 2, 8, 1, 4, 3000, 64, "fp16", "bnhd", None, 2.0,
+     True, (256, 0), 5.0),
+    ("bf16_window_noncausal_right", 1, 4, 4, 3, 800, 128, "bf16", "bhnd", (2, 800), 1.0,
+     False, (100, 1), 0.0),
+    ("bf16_softcap_decode", 2, 16, 2, 2, 4000, 128, "bf16", "bhnd", None, 2.5,
+     True, (-1, -1), 30.0),
+]
+
+
+@pytest.mark.parametrize("case", DEC, ids=[c[0] for c in DEC])
+def test_local_decode(gpu_lib, case):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, layout, lens, std, causal, window, cap = case
+    _say(f"[local-decode] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     qk_std=std, lens=lens)
+    t = _dev(x, w, layout)
+    o, lse = bd.attn_decode(t["q"], t["k"], t["v"], layout=layout, causal=causal,
+                            kv_lens=t["lens"], window_size=window, softcap=cap)
+    torch.cuda.synchronize()
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], causal=causal,
+                           window=window, softcap=cap, bottom_right=True)
+    check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
+
+
+# ------------------------------------------------------------- full workloads
+def _workload_rows(name, n_heads=6, n_rows=32):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    w = inputs.WORKLOADS[name]
+    _say(f"[local-workload] {name}: inputs")
+    x = inputs.make_inputs(w, with_do=False)
+    t = _dev(x, w, "bhnd")
+    opts = dict(window=w.window, grid=w.grid, softcap=w.softcap or None)
+    _say(f"[local-workload] {name}: GPU")
+    o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["lens"],
+                         window_size=w.window or (-1, -1), grid=w.grid, softcap=w.softcap)
+    torch.cuda.synchronize()
+    oh, lh = host(o), host(lse)
+    rng = np.random.default_rng(5)
+    heads = [(0, 0), (w.B - 1, w.Hq - 1)] + [
+        (int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n_heads - 2)]
+    for (b, h) in heads:
+        rows = sorted(set(rng.choice(w.Nq, size=n_rows, replace=False).tolist())
+                      | {0, w.Nq - 1, w.Nq // 2})
+        O_ref, L_ref = ref_fwd_rows(x["q"], x["k"], x["v"], b, h, rows, causal=w.causal,
+                                    kv_lens=x["kv_lens"], **{k: v for k, v in opts.items() if v})
+        check_out(oh[b, h, rows], lh[b, h, rows], O_ref, L_ref, w.dtype, f"{name} b{b} h{h}")
+    assert bool(torch.isfinite(lse).all())
+
+
+def test_workload_vit_softcap(gpu_lib):
+    _workload_rows("vit_softcap_bf16_b8_h12_n3136_d64")
+
+
+def test_workload_vit_neighbourhood(gpu_lib):
+    _workload_rows("vit_nbr_bf16_b8_h12_n3136_d64")
+
+
+def test_workload_window_decode(gpu_lib):
+    """The sliding-window decode workload: every row against the oracle."""
+    import torch
+    from exact_attention_25_amd import binding as bd
+    w = inputs.WORKLOADS["decode_window_bf16_b8_hq32_kv8_q1_nk32768_d128"]
+    _say(f"[local-decode] {w.name}")
+    x = inputs.make_inputs(w, with_do=False)
+    t = _dev(x, w, "bhnd")
+    o, lse = bd.attn_decode(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["lens"],
+                            window_size=w.window)
+    torch.cuda.synchronize()
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], kv_lens=x["kv_lens"], causal=w.causal,
+                           window=w.window, bottom_right=True)
+    check_out(host(o), lse, O_ref, L_ref, w.dtype, w.name)
