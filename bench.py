@@ -183,22 +183,26 @@ def cpu_baseline(w, x, budget_s=15.0, backward=False, decode=False):
     G = w.Hq // w.Hkv
     done = 0
     t0 = time.perf_counter()
+    mods = {k: v for k, v in (("window", w.window), ("grid", w.grid),
+                              ("softcap", w.softcap or None)) if v}
     if backward:
         # one (batch, kv-head) group per oracle call: G heads
+        flops = 0.0
         for b in range(w.B):
+            lens = None if x["kv_lens"] is None else x["kv_lens"][b:b + 1]
+            per_head = (10.0 * w.d * acc.local_pairs(w.Nq, lens, 1, w.causal, w.window, w.grid)
+                        if is_local(w) else acc.bwd_flops(1, 1, w.Nq, w.Nk, w.d, w.causal))
             for g in range(w.Hkv):
                 ref_bwd_group(x["q"], x["k"], x["v"], x["do"], b, g, causal=w.causal,
-                              kv_lens=x["kv_lens"])
+                              kv_lens=x["kv_lens"], **mods)
                 done += G
+                flops += G * per_head
                 if time.perf_counter() - t0 >= budget_s:
                     break
             if time.perf_counter() - t0 >= budget_s:
                 break
-        flops = acc.bwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
         what = "fp64 numpy oracle backward (incl. its forward)"
     else:
-        mods = {k: v for k, v in (("window", w.window), ("grid", w.grid),
-                                  ("softcap", w.softcap or None)) if v}
         if decode:
             mods["bottom_right"] = True
         flops = 0.0
@@ -360,8 +364,10 @@ def main():
             w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, bd.ATTN_BF16 if w.dtype == "bf16" else bd.ATTN_FP16,
             causal=w.causal)), dtype=torch.uint8, device=device)
         fn = lambda: bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w.causal,
-                                 kv_lens=t["kv_lens"], workspace=ws)
-        flops = acc.bwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+                                 kv_lens=t["kv_lens"], workspace=ws, **lkw)
+        # 10 d FLOPs per pair and head against the forward's 4 d
+        flops = (2.5 * fwd_flops_of(w, x["kv_lens"]) if is_local(w)
+                 else acc.bwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal))
     else:
         fn = fwd
         flops = fwd_flops_of(w, x["kv_lens"])
@@ -412,7 +418,9 @@ def main():
         print(json.dumps(rec), flush=True)
         return
     metric = METRIC
-    if bwd:
+    if bwd and is_local(w):
+        metric = "attention bwd TFLOPS (10*d FLOPs per visible (query, key) pair and head)"
+    elif bwd:
         metric = "attention bwd TFLOPS (10*B*H*N^2*d, halved for causal)"
     elif is_local(w):
         metric = "attention fwd TFLOPS (4*d FLOPs per visible (query, key) pair and head)"

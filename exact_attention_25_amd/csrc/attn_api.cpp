@@ -96,7 +96,7 @@ attn_status attn_validate(const attn_params* p, int for_backward) {
   const attn_status sl = validate_local(p);
   if (sl != ATTN_OK) return sl;
   if (p->d < 8 || p->d > 128 || p->d % 8 != 0) return ATTN_EUNSUPPORTED;
-  if (for_backward && (is_local(p) || p->softcap > 0.0f)) return ATTN_EUNSUPPORTED;
+  (void)for_backward;   // the backward takes everything the forward takes
   return ATTN_OK;
 }
 
@@ -235,10 +235,16 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.scale = resolve_scale(p);
   a.c = a.scale * kLog2eF;
   a.grad_f32 = grad_dtype == ATTN_FP32 ? 1 : 0;
+  a.loc = local_vis(p);
+  softcap_consts(p, &a.cap_a, &a.cap_c2);
+  attn::FwdMode m;
+  m.local = is_local(p);
+  m.causal = p->causal != 0 && !m.local;   // folded into the window when local
+  m.mask = p->mask != nullptr;
+  m.softcap = p->softcap > 0.0f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = p->dtype == ATTN_FP32
-                           ? attn::launch_bwd32(a, p->causal != 0, s)
-                           : attn::launch_bwd16(a, p->dtype == ATTN_BF16, p->causal != 0, s);
+  const hipError_t e = p->dtype == ATTN_FP32 ? attn::launch_bwd32(a, m, s)
+                                             : attn::launch_bwd16(a, p->dtype == ATTN_BF16, m, s);
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 

@@ -1,8 +1,9 @@
 // Backward attention: kernel instances, work split and dispatch (the kernels
-// are in attn_bwd_kernel.h).
+// are in attn_bwd_kernel.h; the local and soft-capped instances are built in
+// the attn_bwd_var_*.hip files).
 #include <type_traits>
 
-#include "attn_bwd_kernel.h"
+#include "attn_bwd_variants.h"
 
 namespace attn {
 
@@ -38,9 +39,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int64_t n8q, i
 }
 
 template <class E, int D>
-static hipError_t launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
-  constexpr int NW_KV = kBwdKeysPerBlock / 32, BR = 128;
-  constexpr int NW_Q = 4, BC = 128;
+static hipError_t launch_bwd_t(const BwdArgs& a, FwdMode m, hipStream_t st) {
   if (std::is_same<E, BF16>::value) {
     const int64_t n8q = (int64_t)a.B * a.Hq * a.Nq * a.d / 8;
     const int64_t n8k = (int64_t)a.B * a.Hkv * a.Nk * a.d / 8;
@@ -50,46 +49,31 @@ static hipError_t launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
       hipLaunchKernelGGL(bwd_prep_kernel, dim3(blocks), dim3(256), 0, st, a, n8q, n8k);
     }
   }
-  // dQ, and D / nl2 per row for the dK/dV pass
-  if (a.Nq > 0) {
-    const int nqb = (a.Nq + NW_Q * 32 - 1) / (NW_Q * 32);
-    dim3 grid((unsigned)(a.B * a.Hq * nqb)), block(NW_Q * 64);
-    if (a.mask) {
-      if (causal) hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, true, true>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, false, true>), grid, block, 0, st, a);
-    } else {
-      if (causal) hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, true, false>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((bwd_q_kernel<E, D, NW_Q, BC, false, false>), grid, block, 0, st, a);
-    }
+  if (m.local || m.softcap) {
+    launch_bwd_variant<E, D>(a, m, st);
+  } else if (m.mask) {
+    if (m.causal) launch_bwd_qkv<E, D, true, true, false, false>(a, st);
+    else launch_bwd_qkv<E, D, false, true, false, false>(a, st);
+  } else {
+    if (m.causal) launch_bwd_qkv<E, D, true, false, false, false>(a, st);
+    else launch_bwd_qkv<E, D, false, false, false, false>(a, st);
   }
-  // dK / dV (after dQ: it reads D and nl2)
-  if (a.Nk > 0) {
-    const int nkb = (a.Nk + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock;
-    dim3 grid((unsigned)(a.B * a.Hkv * a.kv_chunks * nkb)), block(NW_KV * 64);
-    if (a.mask) {
-      if (causal) hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, true, true>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, false, true>), grid, block, 0, st, a);
-    } else {
-      if (causal) hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, true, false>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((bwd_kv_kernel<E, D, NW_KV, BR, false, false>), grid, block, 0, st, a);
-    }
-    if (a.kv_chunks > 1) {
-      const int64_t n = (int64_t)a.B * a.Hkv * a.Nk * a.d;
-      const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
-      hipLaunchKernelGGL((bwd_kv_reduce_kernel<typename E::T>), dim3(blocks), dim3(256), 0, st, a);
-    }
+  if (a.Nk > 0 && a.kv_chunks > 1) {
+    const int64_t n = (int64_t)a.B * a.Hkv * a.Nk * a.d;
+    const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+    hipLaunchKernelGGL((bwd_kv_reduce_kernel<typename E::T>), dim3(blocks), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
 template <class E>
-static hipError_t launch_bwd_e(const BwdArgs& a, bool causal, hipStream_t st) {
-  if (a.d > 64) return launch_bwd_t<E, 128>(a, causal, st);
-  return launch_bwd_t<E, 64>(a, causal, st);
+static hipError_t launch_bwd_e(const BwdArgs& a, FwdMode m, hipStream_t st) {
+  if (a.d > 64) return launch_bwd_t<E, 128>(a, m, st);
+  return launch_bwd_t<E, 64>(a, m, st);
 }
 
-hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, bool causal, hipStream_t st) {
-  return is_bf16 ? launch_bwd_e<BF16>(a, causal, st) : launch_bwd_e<FP16>(a, causal, st);
+hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st) {
+  return is_bf16 ? launch_bwd_e<BF16>(a, m, st) : launch_bwd_e<FP16>(a, m, st);
 }
 
 }  // namespace attn

@@ -18,8 +18,15 @@
 // LDS tiles use a row stride of D+1 floats.  MFMA operand layouts (32x32x2):
 // lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; register r of the
 // result holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+//
+// LOCAL (window / 2-D neighbourhood, causal folded in) and SOFTCAP as in the
+// 16-bit kernels (attn_bwd_kernel.h): tiles outside a block's reach are
+// skipped, excluded elements get P = 0 from the visibility words of
+// local_mask.h, and the soft cap's logit and derivative come from
+// softcap_grad.
 #include "attn_kernels.h"
 #include "device_common.h"
+#include "local_mask.h"
 
 namespace attn {
 
@@ -43,7 +50,7 @@ __global__ __launch_bounds__(256) void bwd32_prep_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool LOCAL, bool SOFTCAP>
 __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
   constexpr int BC = 32, NW = 4, ROWS = NW * 32, DT = D / 32, KS = D / 2, LD = D + 1;
   __shared__ float ks_[BC * LD];
@@ -69,7 +76,22 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
   if (a.kv_lens) kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
   int kv_end = kv_limit;
   if (CAUSAL) kv_end = min(kv_end, min(q_blk0 + ROWS, a.Nq));
-  const int n_tiles = (kv_end + BC - 1) / BC;
+  int t_begin = 0, t_end = (kv_end + BC - 1) / BC;
+  int w_lo = 0, w_hi = t_end;   // this wave's key tiles
+  LocalVis::Row lrow{};
+  if constexpr (LOCAL) {
+    int lo, hi;
+    a.loc.key_range(q_blk0, min(q_blk0 + ROWS, a.Nq) - 1, kv_limit, lo, hi);
+    t_begin = lo / BC;
+    t_end = hi >= lo ? hi / BC + 1 : t_begin;
+    w_lo = w_hi = 0;
+    if (q_w0 < a.Nq) {
+      a.loc.key_range(q_w0, min(q_w0 + 31, a.Nq - 1), kv_limit, lo, hi);
+      w_lo = lo / BC;
+      w_hi = hi >= lo ? hi / BC + 1 : w_lo;
+    }
+    lrow = a.loc.row(crow);
+  }
 
   const float* qp = (const float*)a.q + b * a.q_sb + h * a.q_sh + (int64_t)crow * a.q_sn;
   const float* dop = (const float*)a.dout + b * a.q_sb + h * a.q_sh + (int64_t)crow * a.q_sn;
@@ -93,7 +115,7 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = t_begin; j < t_end; ++j) {
     const int j0 = j * BC;
     __syncthreads();
     for (int idx = threadIdx.x; idx < BC * D; idx += NW * 64) {
@@ -103,6 +125,13 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
       vs_[r * LD + c] = c < a.d ? vp[grow * a.k_sn + c] : 0.f;
     }
     __syncthreads();
+    uint32_t w = 0;   // LOCAL: bit 8 (r / 4) + r % 4 set iff register r's key is visible
+    if constexpr (LOCAL) {
+      if (j < w_lo || j >= w_hi) continue;
+      const uint32_t bits = (uint32_t)a.loc.bits(lrow, j0, kv_limit);
+      if (!__builtin_amdgcn_ballot_w64(bits != 0)) continue;
+      w = bits >> (4 * hl);
+    }
 
     // S^T = K Q^T and dP^T = V dO^T: lane holds row qrow, register r key
     // j0 + 8 (r / 4) + 4 hl + r % 4
@@ -117,9 +146,16 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + (r >> 2) * 8 + hl * 4 + (r & 3);
       const float ml = MASK ? __builtin_fmaf(mrow[min(key, a.Nk - 1)], kLog2e, nl2) : nl2;
-      float p = fast_exp2(__builtin_fmaf(s[r], a.c, ml));
-      if (key >= kv_limit || (CAUSAL && key > qrow)) p = 0.f;
-      ds[r] = p * (dp[r] - dd);
+      float g = 1.f;
+      const float t = SOFTCAP ? softcap_grad(s[r], a.cap_a, a.cap_c2, g) + ml
+                              : __builtin_fmaf(s[r], a.c, ml);
+      float p = fast_exp2(t);
+      if constexpr (LOCAL) {
+        if (!((w >> ((r >> 2) * 8 + (r & 3))) & 1u)) p = 0.f;
+      } else {
+        if (key >= kv_limit || (CAUSAL && key > qrow)) p = 0.f;
+      }
+      ds[r] = SOFTCAP ? p * g * (dp[r] - dd) : p * (dp[r] - dd);
     }
     // dQ^T += K^T dS^T, two keys per step (lane half hl supplies key
     // 8 (r / 4) + 4 hl + r % 4 of the tile through register r)
@@ -148,7 +184,7 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool LOCAL, bool SOFTCAP>
 __global__ __launch_bounds__(256) void bwd32_kv_kernel(BwdArgs a) {
   constexpr int BR = 32, NW = 4, KEYS = NW * 32, DT = D / 32, KS = D / 2, LD = D + 1;
   __shared__ float qs_[BR * LD];
@@ -192,7 +228,23 @@ __global__ __launch_bounds__(256) void bwd32_kv_kernel(BwdArgs a) {
   }
 
   // rows before key0 see none of this block's keys (causal)
-  const int q_start = CAUSAL ? (key0 / BR) * BR : 0;
+  int q_start = CAUSAL ? (key0 / BR) * BR : 0;
+  int q_end = a.Nq;
+  int wq_lo = 0, wq_hi = a.Nq - 1;   // rows that may see one of this wave's keys
+  LocalVis lvt{};
+  LocalVis::Row lrow{};
+  if constexpr (LOCAL) {
+    // the rows that see key j are those the exchanged relation gives for j
+    lvt = a.loc.transposed();
+    int lo, hi;
+    lvt.key_range(key0, min(key0 + KEYS, kv_limit) - 1, a.Nq, lo, hi);
+    q_start = (lo / BR) * BR;
+    q_end = hi >= lo ? hi + 1 : q_start;
+    wq_lo = 1;
+    wq_hi = 0;
+    if (kw0 < kv_limit) lvt.key_range(kw0, min(kw0 + 31, kv_limit - 1), a.Nq, wq_lo, wq_hi);
+    lrow = lvt.row(ckey);
+  }
   const bool any = key0 < kv_limit;
   for (int hh = 0; hh < a.group && any; ++hh) {
     const int h = g * a.group + hh;
@@ -200,7 +252,7 @@ __global__ __launch_bounds__(256) void bwd32_kv_kernel(BwdArgs a) {
     const float* dop = (const float*)a.dout + b * a.q_sb + h * a.q_sh;
     const float* mcol = MASK ? a.mask + b * a.m_sb + h * a.m_sh + ckey : nullptr;
     const int64_t wbase = ((int64_t)b * a.Hq + h) * a.ld_rows;
-    for (int q0 = q_start; q0 < a.Nq; q0 += BR) {
+    for (int q0 = q_start; q0 < q_end; q0 += BR) {
       __syncthreads();
       for (int idx = threadIdx.x; idx < BR * D; idx += NW * 64) {
         const int r = idx / D, c = idx % D;
@@ -214,6 +266,13 @@ __global__ __launch_bounds__(256) void bwd32_kv_kernel(BwdArgs a) {
         dds_[threadIdx.x] = a.delta[wbase + q0 + threadIdx.x];
       }
       __syncthreads();
+      uint32_t w = 0;   // LOCAL: bit 8 (r / 4) + r % 4 set iff register r's row sees the key
+      if constexpr (LOCAL) {
+        if (q0 + BR - 1 < wq_lo || q0 > wq_hi) continue;
+        const uint32_t bits = (uint32_t)lvt.bits(lrow, q0, a.Nq);
+        if (!__builtin_amdgcn_ballot_w64(bits != 0)) continue;
+        w = bits >> (4 * hl);
+      }
 
       // S = Q K^T and dP = dO V^T: lane holds key `key`, register r row
       // q0 + 8 (r / 4) + 4 hl + r % 4
@@ -231,10 +290,17 @@ __global__ __launch_bounds__(256) void bwd32_kv_kernel(BwdArgs a) {
         const float ml = MASK ? __builtin_fmaf(mcol[(int64_t)min(row, a.Nq - 1) * a.m_sq], kLog2e,
                                                nls_[lr])
                               : nls_[lr];
-        float p = fast_exp2(__builtin_fmaf(s[r], a.c, ml));
-        if (CAUSAL && key > row) p = 0.f;
+        float g = 1.f;
+        const float t = SOFTCAP ? softcap_grad(s[r], a.cap_a, a.cap_c2, g) + ml
+                                : __builtin_fmaf(s[r], a.c, ml);
+        float p = fast_exp2(t);
+        if constexpr (LOCAL) {
+          if (!((w >> ((r >> 2) * 8 + (r & 3))) & 1u)) p = 0.f;
+        } else {
+          if (CAUSAL && key > row) p = 0.f;
+        }
         pv[r] = p;
-        dsv[r] = p * (dp[r] - dds_[lr]);
+        dsv[r] = SOFTCAP ? p * g * (dp[r] - dds_[lr]) : p * (dp[r] - dds_[lr]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS, two rows per step
 #pragma unroll
@@ -268,39 +334,52 @@ __global__ __launch_bounds__(256) void bwd32_kv_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool LOCAL, bool SOFTCAP>
 static void launch_bwd32_t(const BwdArgs& a, hipStream_t st) {
   if (a.Nq > 0) {
     const int nqb = (a.Nq + 127) / 128;
-    hipLaunchKernelGGL((bwd32_q_kernel<D, CAUSAL, MASK>), dim3((unsigned)(a.B * a.Hq * nqb)),
-                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd32_q_kernel<D, CAUSAL, MASK, LOCAL, SOFTCAP>),
+                       dim3((unsigned)(a.B * a.Hq * nqb)), dim3(256), 0, st, a);
   }
   if (a.Nk > 0) {
     const int nkb = (a.Nk + 127) / 128;
-    hipLaunchKernelGGL((bwd32_kv_kernel<D, CAUSAL, MASK>), dim3((unsigned)(a.B * a.Hkv * nkb)),
-                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd32_kv_kernel<D, CAUSAL, MASK, LOCAL, SOFTCAP>),
+                       dim3((unsigned)(a.B * a.Hkv * nkb)), dim3(256), 0, st, a);
+  }
+}
+
+// causal is folded into a.loc under LOCAL
+template <int D, bool MASK, bool LOCAL, bool SOFTCAP>
+static void launch_bwd32_c(const BwdArgs& a, bool causal, hipStream_t st) {
+  if (causal && !LOCAL) launch_bwd32_t<D, !LOCAL, MASK, LOCAL, SOFTCAP>(a, st);
+  else launch_bwd32_t<D, false, MASK, LOCAL, SOFTCAP>(a, st);
+}
+
+template <int D, bool MASK>
+static void launch_bwd32_m(const BwdArgs& a, FwdMode m, hipStream_t st) {
+  if (m.local) {
+    if (m.softcap) launch_bwd32_c<D, MASK, true, true>(a, false, st);
+    else launch_bwd32_c<D, MASK, true, false>(a, false, st);
+  } else {
+    if (m.softcap) launch_bwd32_c<D, MASK, false, true>(a, m.causal, st);
+    else launch_bwd32_c<D, MASK, false, false>(a, m.causal, st);
   }
 }
 
 template <int D>
-static void launch_bwd32_d(const BwdArgs& a, bool causal, hipStream_t st) {
-  if (a.mask) {
-    if (causal) launch_bwd32_t<D, true, true>(a, st);
-    else launch_bwd32_t<D, false, true>(a, st);
-  } else {
-    if (causal) launch_bwd32_t<D, true, false>(a, st);
-    else launch_bwd32_t<D, false, false>(a, st);
-  }
+static void launch_bwd32_d(const BwdArgs& a, FwdMode m, hipStream_t st) {
+  if (m.mask) launch_bwd32_m<D, true>(a, m, st);
+  else launch_bwd32_m<D, false>(a, m, st);
 }
 
-hipError_t launch_bwd32(const BwdArgs& a, bool causal, hipStream_t st) {
+hipError_t launch_bwd32(const BwdArgs& a, FwdMode m, hipStream_t st) {
   const int64_t n = (int64_t)a.B * a.Hq * a.ld_rows;
   if (n > 0) {
     const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     hipLaunchKernelGGL(bwd32_prep_kernel, dim3(blocks), dim3(256), 0, st, a);
   }
-  if (a.d > 64) launch_bwd32_d<128>(a, causal, st);
-  else launch_bwd32_d<64>(a, causal, st);
+  if (a.d > 64) launch_bwd32_d<128>(a, m, st);
+  else launch_bwd32_d<64>(a, m, st);
   return hipGetLastError();
 }
 

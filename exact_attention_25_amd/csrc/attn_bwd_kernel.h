@@ -44,6 +44,15 @@
 // elsewhere, so P = 0 and dS = 0 there; other tiles start from the MFMA's
 // zero operand.  The dK/dV kernel leaves keys past kv_lens unmasked: their
 // P and dS reach only their own rows of dK and dV, which it stores as zero.
+//
+// Local attention (LOCAL: window and/or 2-D neighbourhood, causal folded into
+// the window; local_mask.h) uses the same start pattern, taken from the
+// 64-bit visibility words of the lane's row (dQ kernel) or, with queries and
+// keys exchanged, of its key (dK/dV kernel); tiles outside a block's reach
+// are skipped whole.  SOFTCAP recomputes the capped logit
+// t = cap tanh(scale s / cap) (in log2 units) for P and multiplies dS by the
+// cap's derivative 1 - tanh^2 = 4 r (1 - r), r = 1 / (1 + e^(2 scale s / cap));
+// a masked score (-inf) is kept at -inf, since the cap would map it to -cap.
 #pragma once
 
 #include <type_traits>
@@ -51,9 +60,11 @@
 
 #include "attn_kernels.h"
 #include "device_common.h"
+#include "local_mask.h"
 
 
 namespace attn {
+
 
 // 8 x 16-bit input values -> 8 x fp16 (identity for fp16 inputs).
 template <class E>
@@ -195,8 +206,11 @@ using BwdTile = typename std::conditional<D == 128, SwzTile<R, NW>, PadTile<R, D
 //   A^T += K^T X^T, B^T += K^T P^T    32x32x16 fp16 MFMA, K^T read transposed
 //                                     from LDS, X^T / P^T from registers
 // Epilogue: dQ = scale (A - D B); D and nl2 to the workspace.
-template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
+template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK, bool LOCAL = false,
+          bool SOFTCAP = false>
 struct BwdQ {
+  static_assert(!(LOCAL && CAUSAL), "causal masking is part of the window under LOCAL");
+  static_assert(!LOCAL || BC == 128, "LOCAL masks a tile through two 64-bit words");
   using TL = BwdTile<BC, D, NW>;
   static constexpr int ROWS = NW * 32;
   static constexpr int KB = BC / 32;
@@ -220,6 +234,9 @@ struct BwdQ {
     float c, nl2;
     const float* mrow;          // additive mask row of this lane's query (MASK)
     int nk1;                    // Nk - 1
+    int t_lo, t_hi;             // LOCAL: this wave's key tiles [t_lo, t_hi)
+    LocalVis::Row lrow;         // LOCAL: this lane's query position
+    float cap_a, cap_c2;        // SOFTCAP constants
     H8 qf[KS];
     V8 df[KS];
     f32x16 acc_a[DT], acc_b[DT];
@@ -280,6 +297,7 @@ struct BwdQ {
     int lim;                    // keys with offset > lim are masked (see pipe_slot)
     bool msk;                   // the tile has masked keys for this wave
     int j0;                     // first key of the tile
+    uint32_t lw[KB];            // LOCAL: visibility words per key block (bit 8 (r/4) + r%4)
     float mv[KB][16];           // additive mask values per key block (MASK)
     f32x16 s, dp;
     H8 pf[2][2], xf[2][2];
@@ -315,10 +333,21 @@ struct BwdQ {
     for (int e = 0; e < 4; ++e) {
       // P = exp2(s c + mask log2(e) - LSE log2(e))
       const float ml = MASK ? __builtin_fmaf(c.mv[K][GQ * 4 + e], kLog2e, st.nl2) : st.nl2;
-      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, ml));
-      pv[e] = p;
-      xv[e] = p * c.dp[GQ * 4 + e];
-      st.dsum[e] += xv[e];
+      if constexpr (SOFTCAP) {
+        // D sums P dP; the products take P g and P g dP (dS = P g (dP - D))
+        float g;
+        const float t = softcap_grad(c.s[GQ * 4 + e], st.cap_a, st.cap_c2, g);
+        const float p = fast_exp2(t + ml);
+        const float x = p * c.dp[GQ * 4 + e];
+        st.dsum[e] += x;
+        pv[e] = p * g;
+        xv[e] = x * g;
+      } else {
+        const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, ml));
+        pv[e] = p;
+        xv[e] = p * c.dp[GQ * 4 + e];
+        st.dsum[e] += xv[e];
+      }
     }
     constexpr int t2 = GQ >> 1, half = (GQ & 1) * 4;
     const f16x2 p01 = FP16::cvt2(pv[0], pv[1]), p23 = FP16::cvt2(pv[2], pv[3]);
@@ -354,12 +383,17 @@ struct BwdQ {
         // row (causal) or past kv_limit: register r holds key
         // j0 + 32 k + 4 hl + 8 (r / 4) + r % 4, visible iff
         // 32 k + 8 (r / 4) + r % 4 <= lim; 0 elsewhere.  Other tiles start
-        // from the MFMA's zero operand.
+        // from the MFMA's zero operand.  LOCAL: the same from the
+        // visibility word of key block k.
         if (c.msk) {
           f32x16 init;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            init[r] = (k * 32 + (r >> 2) * 8 + (r & 3) <= c.lim) ? 0.f : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (LOCAL)
+              init[r] = keep_if_bit(0.f, c.lw[k], (r >> 2) * 8 + (r & 3));
+            else
+              init[r] = (k * 32 + (r >> 2) * 8 + (r & 3) <= c.lim) ? 0.f : -INFINITY;
+          }
           c.s = FP16::mfma(c.opd[SL], st.qf[0], init);
         } else {
           c.s = FP16::mfma(c.opd[SL], st.qf[0], f32x16{});
@@ -390,29 +424,47 @@ struct BwdQ {
                                                        std::integer_sequence<int, SL...>) {
     (pipe_load<SL>(st, c), ...);
   }
+  // bits: LOCAL visibility of keys j0..j0+63 and j0+64..j0+127 for this
+  // lane's row
   template <int PF>
   static __device__ __forceinline__ void pipe_tile(State& st, const char* kc, const char* vc,
-                                                   int j0) {
+                                                   int j0, uint64_t b0, uint64_t b1) {
     Pipe c;
     c.kc = kc;
     c.vc = vc;
-    const int base = j0 + 4 * st.hl;
-    c.lim = st.kv_limit - 1 - base;
-    if (CAUSAL) c.lim = min(c.lim, st.qrow - base);
-    c.msk = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
+    if constexpr (LOCAL) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        c.lw[k] = (uint32_t)(((k < 2) ? b0 : b1) >> ((k & 1) * 32 + 4 * st.hl));
+      c.msk = __builtin_amdgcn_ballot_w64((b0 & b1) != ~0ull) != 0;
+    } else {
+      const int base = j0 + 4 * st.hl;
+      c.lim = st.kv_limit - 1 - base;
+      if (CAUSAL) c.lim = min(c.lim, st.qrow - base);
+      c.msk = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
+    }
     c.j0 = j0;
     pipe_prologue(st, c, std::make_integer_sequence<int, PF>{});
     pipe_slots<PF>(st, c, std::make_integer_sequence<int, NSLOT>{});
   }
 
   // Iteration j: tile j is in (kc, vc); tile j+1 goes into (kn, vn).
-  static __device__ __forceinline__ void step(State& st, int j, int n, int n_act, char* kc,
-                                              const char* vc, char* kn, char* vn) {
+  static __device__ __forceinline__ void step(const BwdArgs& a, State& st, int j, int n,
+                                              int n_act, char* kc, const char* vc, char* kn,
+                                              char* vn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < n) issue(st, j + 1, kn, vn);
-    if (j >= n_act) return;
-    pipe_tile<PF>(st, kc, vc, j * BC);
+    if constexpr (LOCAL) {
+      if (j < st.t_lo || j >= st.t_hi) return;
+      const uint64_t b0 = a.loc.bits(st.lrow, j * BC, st.kv_limit);
+      const uint64_t b1 = a.loc.bits(st.lrow, j * BC + 64, st.kv_limit);
+      if (!__builtin_amdgcn_ballot_w64((b0 | b1) != 0)) return;   // no visible key
+      pipe_tile<PF>(st, kc, vc, j * BC, b0, b1);
+    } else {
+      if (j >= n_act) return;
+      pipe_tile<PF>(st, kc, vc, j * BC, 0, 0);
+    }
   }
 
   static __device__ void run(const BwdArgs& a, char* k0, char* v0, char* k1, char* v1) {
@@ -456,6 +508,8 @@ struct BwdQ {
     st.nk1 = a.Nk - 1;
     if (MASK) st.mrow = a.mask + b * a.m_sb + h * a.m_sh + (int64_t)crow * a.m_sq;
     st.c = a.c;
+    st.cap_a = a.cap_a;
+    st.cap_c2 = a.cap_c2;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       st.acc_a[dt] = f32x16{};
@@ -474,11 +528,26 @@ struct BwdQ {
       st.off[i] = TL::offset(i * NW + st.wave, st.lane, dchunks, a.k_sn);
     st.lb = TL::bases(st.lane);
 
-    if (n_tiles > 0) issue(st, 0, k0, v0);
-    for (int j = 0; j < n_tiles; j += 2) {
-      step(st, j, n_tiles, n_act, k0, v0, k1, v1);
-      if (j + 1 >= n_tiles) break;
-      step(st, j + 1, n_tiles, n_act, k1, v1, k0, v0);
+    // key tiles [t_begin, t_end) pass through LDS
+    int t_begin = 0, t_end = n_tiles;
+    if constexpr (LOCAL) {
+      int lo, hi;
+      a.loc.key_range(q_blk0, min(q_blk0 + ROWS, a.Nq) - 1, st.kv_limit, lo, hi);
+      t_begin = lo / BC;
+      t_end = hi >= lo ? hi / BC + 1 : t_begin;
+      st.t_lo = st.t_hi = 0;
+      if (st.q_w0 < a.Nq) {
+        a.loc.key_range(st.q_w0, min(st.q_w0 + 31, a.Nq - 1), st.kv_limit, lo, hi);
+        st.t_lo = lo / BC;
+        st.t_hi = hi >= lo ? hi / BC + 1 : st.t_lo;
+      }
+      st.lrow = a.loc.row(crow);
+    }
+    if (t_begin < t_end) issue(st, t_begin, k0, v0);
+    for (int j = t_begin; j < t_end; j += 2) {
+      step(a, st, j, t_end, n_act, k0, v0, k1, v1);
+      if (j + 1 >= t_end) break;
+      step(a, st, j + 1, t_end, n_act, k1, v1, k0, v0);
     }
 
     const float dtot = add_with_other_half((st.dsum[0] + st.dsum[1]) + (st.dsum[2] + st.dsum[3]));
@@ -512,9 +581,10 @@ struct BwdQ {
   }
 };
 
-template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK>
+template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK, bool LOCAL = false,
+          bool SOFTCAP = false>
 __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(BwdArgs a) {
-  using K = BwdQ<E, D, NW, BC, CAUSAL, MASK>;
+  using K = BwdQ<E, D, NW, BC, CAUSAL, MASK, LOCAL, SOFTCAP>;
   __shared__ __attribute__((aligned(1024))) char k0[K::TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::TL::BYTES];
@@ -534,8 +604,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(BwdArgs a) {
 //   dV += P^T dO, dK += dS^T Q   32x32x16 MFMA, A = P^T / dS^T from the same
 //                                registers (query slots matched), B = dO / Q
 //                                read transposed from LDS
-template <class E, int D, int NW, int BR, bool CAUSAL, bool MASK>
+template <class E, int D, int NW, int BR, bool CAUSAL, bool MASK, bool LOCAL = false,
+          bool SOFTCAP = false>
 struct BwdKV {
+  static_assert(!(LOCAL && CAUSAL), "causal masking is part of the window under LOCAL");
+  static_assert(!LOCAL || BR == 128, "LOCAL masks a tile through two 64-bit words");
   using TL = BwdTile<BR, D, NW>;
   static constexpr int KEYS = NW * 32;
   static constexpr int QB = BR / 32;
@@ -562,6 +635,10 @@ struct BwdKV {
     uint32_t off[TL::IPW];
     float c;
     int nq1;                    // Nq - 1
+    int wq_lo, wq_hi;           // LOCAL: rows that may see one of this wave's keys
+    LocalVis lvt;               // LOCAL: the visibility with queries and keys exchanged
+    LocalVis::Row lrow;         // LOCAL: this lane's key, as a position of lvt
+    float cap_a, cap_c2;        // SOFTCAP constants
     H8 kf[KS], vf[KS];
     f32x16 dk[DT], dv[DT];
   };
@@ -632,6 +709,7 @@ struct BwdKV {
     int dlt;                    // key - qt0 - 4 hl (causal mask)
     bool msk;                   // causal: the tile crosses this wave's diagonal
     int qt0;                    // first row of the tile
+    uint32_t lw[QB];            // LOCAL: visibility words per sub-block (bit 8 (r/4) + r%4)
     const float* mcol;          // additive mask column of this lane's key, tile's head (MASK)
     int64_t msq;                // mask row stride
     float mv[QB][16];           // additive mask values per sub-block (MASK)
@@ -669,9 +747,17 @@ struct BwdKV {
     for (int e = 0; e < 4; ++e) {
       // P = exp2(s c + mask log2(e) - LSE log2(e))
       const float ml = MASK ? __builtin_fmaf(c.mv[I][GQ * 4 + e], kLog2e, nl[e]) : nl[e];
-      const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, ml));
-      pv[e] = p;
-      dsv[e] = p * (c.dp[GQ * 4 + e] - dd[e]);
+      if constexpr (SOFTCAP) {
+        float g;
+        const float t = softcap_grad(c.s[GQ * 4 + e], st.cap_a, st.cap_c2, g);
+        const float p = fast_exp2(t + ml);
+        pv[e] = p;
+        dsv[e] = p * g * (c.dp[GQ * 4 + e] - dd[e]);
+      } else {
+        const float p = fast_exp2(__builtin_fmaf(c.s[GQ * 4 + e], st.c, ml));
+        pv[e] = p;
+        dsv[e] = p * (c.dp[GQ * 4 + e] - dd[e]);
+      }
     }
     constexpr int t2 = GQ >> 1, half = (GQ & 1) * 4;
     const f16x2 p01 = FP16::cvt2(pv[0], pv[1]), p23 = FP16::cvt2(pv[2], pv[3]);
@@ -708,11 +794,16 @@ struct BwdKV {
         // key - qt0 - 4 hl <= 32 i + 8 (r / 4) + r % 4 for register r), so
         // that P = 0 and dS = 0 there; 0 elsewhere.  Other tiles start from
         // the MFMA's zero operand.
-        if (CAUSAL && c.msk) {
+        // LOCAL: the same from the visibility word of sub-block i.
+        if ((CAUSAL || LOCAL) && c.msk) {
           f32x16 init;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            init[r] = (c.dlt <= i * 32 + (r >> 2) * 8 + (r & 3)) ? 0.f : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (LOCAL)
+              init[r] = keep_if_bit(0.f, c.lw[i], (r >> 2) * 8 + (r & 3));
+            else
+              init[r] = (c.dlt <= i * 32 + (r >> 2) * 8 + (r & 3)) ? 0.f : -INFINITY;
+          }
           c.s = FP16::mfma(c.opd[SL], st.kf[0], init);
         } else {
           c.s = FP16::mfma(c.opd[SL], st.kf[0], f32x16{});
@@ -743,15 +834,24 @@ struct BwdKV {
                                                        std::integer_sequence<int, SL...>) {
     (pipe_load<SL>(st, c), ...);
   }
+  // b0, b1 (LOCAL): rows qt0..qt0+63 and qt0+64..qt0+127 that see this
+  // lane's key
   template <int PF>
   static __device__ __forceinline__ void pipe_tile(const BwdArgs& a, State& st, const char* stage,
-                                                   int h, int qt0) {
+                                                   int h, int qt0, uint64_t b0, uint64_t b1) {
     Pipe c;
     c.qc = stage;
     c.dc = stage + TL::BYTES;
     c.sc = stage + 2 * TL::BYTES;
     c.dlt = st.key - qt0 - 4 * st.hl;
-    c.msk = qt0 < st.kw0 + 31;
+    if constexpr (LOCAL) {
+#pragma unroll
+      for (int i = 0; i < QB; ++i)
+        c.lw[i] = (uint32_t)(((i < 2) ? b0 : b1) >> ((i & 1) * 32 + 4 * st.hl));
+      c.msk = __builtin_amdgcn_ballot_w64((b0 & b1) != ~0ull) != 0;
+    } else {
+      c.msk = qt0 < st.kw0 + 31;
+    }
     c.qt0 = qt0;
     if (MASK) {
       c.mcol = a.mask + st.b * a.m_sb + h * a.m_sh + min(st.key, a.Nk - 1);
@@ -773,7 +873,15 @@ struct BwdKV {
     if (CAUSAL && qt0 + BR - 1 < st.kw0) return;         // no row of the tile sees them
     // Keys at or past kv_limit are not masked here: a key's P and dS only
     // reach its own rows of dK / dV, which are stored as zero.
-    pipe_tile<PF>(a, st, cur, hc, qt0);
+    if constexpr (LOCAL) {
+      if (qt0 + BR - 1 < st.wq_lo || qt0 > st.wq_hi) return;
+      const uint64_t b0 = st.lvt.bits(st.lrow, qt0, a.Nq);
+      const uint64_t b1 = st.lvt.bits(st.lrow, qt0 + 64, a.Nq);
+      if (!__builtin_amdgcn_ballot_w64((b0 | b1) != 0)) return;   // no row sees these keys
+      pipe_tile<PF>(a, st, cur, hc, qt0, b0, b1);
+    } else {
+      pipe_tile<PF>(a, st, cur, hc, qt0, 0, 0);
+    }
   }
 
   static __device__ void run(const BwdArgs& a, char* s0, char* s1) {
@@ -817,6 +925,8 @@ struct BwdKV {
       st.dv[dt] = f32x16{};
     }
     st.c = a.c;
+    st.cap_a = a.cap_a;
+    st.cap_c2 = a.cap_c2;
     st.nq1 = a.Nq - 1;
     st.q0p = (const char*)((const _Float16*)a.q16 + b * a.q_sb);
     st.d0p = (const char*)((const _Float16*)a.do16 + b * a.q_sb);
@@ -830,8 +940,21 @@ struct BwdKV {
     st.lb = TL::bases(st.lane);
 
     // query rows that can see some key of this block
-    const int q_start = CAUSAL ? (key0 / BR) * BR : 0;
-    const int n_qt = (key0 < st.kv_limit && q_start < a.Nq) ? (a.Nq - q_start + BR - 1) / BR : 0;
+    int q_start = CAUSAL ? (key0 / BR) * BR : 0;
+    int n_qt = (key0 < st.kv_limit && q_start < a.Nq) ? (a.Nq - q_start + BR - 1) / BR : 0;
+    if constexpr (LOCAL) {
+      st.lvt = a.loc.transposed();
+      int lo, hi;
+      st.lvt.key_range(key0, min(key0 + KEYS, st.kv_limit) - 1, a.Nq, lo, hi);
+      q_start = (lo / BR) * BR;
+      n_qt = (key0 < st.kv_limit && hi >= lo) ? hi / BR + 1 - lo / BR : 0;
+      st.wq_lo = 1;
+      st.wq_hi = 0;
+      if (st.kw0 < st.kv_limit)
+        st.lvt.key_range(st.kw0, min(st.kw0 + 31, st.kv_limit - 1), a.Nq, st.wq_lo, st.wq_hi);
+      st.lrow = st.lvt.row(min(st.key, a.Nk - 1));
+    }
+    const int q_stop = q_start + n_qt * BR;   // rows past the block's reach wrap to the next head
     const int HS = a.group / a.kv_chunks;
     const int h0 = g * a.group + chunk * HS;
     const int n_t = n_qt * HS;   // (head, q-tile) pairs, head-major
@@ -843,7 +966,7 @@ struct BwdKV {
     int hn = h0, qn = q_start;     // head and rows of tile t + 1
     for (int t = 0; t < n_t; t += 2) {
       qn += BR;
-      if (qn >= a.Nq) {
+      if (qn >= q_stop) {
         qn = q_start;
         ++hn;
       }
@@ -852,7 +975,7 @@ struct BwdKV {
       q0 = qn;
       if (t + 1 >= n_t) break;
       qn += BR;
-      if (qn >= a.Nq) {
+      if (qn >= q_stop) {
         qn = q_start;
         ++hn;
       }
@@ -892,9 +1015,10 @@ struct BwdKV {
   }
 };
 
-template <class E, int D, int NW, int BR, bool CAUSAL, bool MASK>
+template <class E, int D, int NW, int BR, bool CAUSAL, bool MASK, bool LOCAL = false,
+          bool SOFTCAP = false>
 __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
-  using K = BwdKV<E, D, NW, BR, CAUSAL, MASK>;
+  using K = BwdKV<E, D, NW, BR, CAUSAL, MASK, LOCAL, SOFTCAP>;
   __shared__ __attribute__((aligned(1024))) char s0[K::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char s1[K::STAGE_BYTES];
   K::run(a, s0, s1);

@@ -64,6 +64,8 @@ struct BwdArgs {
   int32_t grad_f32;      // 1: dq/dk/dv are fp32, 0: input dtype
   int32_t kv_chunks;     // q-head chunks per kv-head in the dK/dV pass
   int32_t ld_rows;       // row stride of delta / nl2 per (b, h): Nq rounded up to 128
+  LocalVis loc;          // window / grid (local launches only)
+  float cap_a, cap_c2;   // soft cap (see FwdArgs)
 };
 
 // Kernel arguments of the split-KV decode (attn_decode.hip).  The Nq new
@@ -117,8 +119,9 @@ hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t s
 // Local / soft-capped 16-bit launches (attn_fwd_local.hip).
 hipError_t launch_fwd16_local(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);
 hipError_t launch_fwd32(const FwdArgs& a, FwdMode m, hipStream_t st);
-hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, bool causal, hipStream_t st);
+// Backward launches take the forward's mode (mode.mask: a.mask is set).
+hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);
 // fp32 backward (attn_bwd32.hip): D from dO and O, then dQ and dK/dV on the fp32 MFMA.
-hipError_t launch_bwd32(const BwdArgs& a, bool causal, hipStream_t st);
+hipError_t launch_bwd32(const BwdArgs& a, FwdMode m, hipStream_t st);
 
 }  // namespace attn

@@ -108,4 +108,16 @@ __device__ __forceinline__ float softcap_log2(float z, float a, float c2) {
   return __builtin_fmaf(-2.0f * a, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * c2)), a);
 }
 
+// The soft cap in the backward: the capped logit (log2 units) of the raw
+// product z and, in g, the cap's derivative factor 1 - tanh^2 = 4 r (1 - r)
+// with r = 1 / (1 + 2^(z c2)) (t = a (1 - 2 r)).  A masked score (z = -inf)
+// stays at -inf, where the cap alone would give -a.
+__device__ __forceinline__ float softcap_grad(float z, float a, float c2, float& g) {
+  const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * c2));
+  const float fr = 4.0f * r;
+  g = __builtin_fmaf(-fr, r, fr);
+  const float t = __builtin_fmaf(-2.0f * a, r, a);
+  return z == -INFINITY ? -INFINITY : t;
+}
+
 }  // namespace attn

@@ -117,9 +117,9 @@ typedef struct {
  * grid_cols > 0 with nbr_rows or nbr_cols < 1, softcap negative or not
  * finite, or so small that 2 * scale * log2(e) / softcap overflows) or
  * ATTN_EUNSUPPORTED (d outside [8, 128] or d % 8 != 0; a window or grid with
- * Nq + Nk >= 2^29; for the backward, a window, grid or soft cap).  B == 0,
- * Nq == 0 and Nk == 0 are valid: the first two make a call a no-op, the last
- * makes every row fully masked. */
+ * Nq + Nk >= 2^29).  The forward and the backward accept the same params.
+ * B == 0, Nq == 0 and Nk == 0 are valid: the first two make a call a no-op,
+ * the last makes every row fully masked. */
 attn_status attn_validate(const attn_params* p, int for_backward);
 
 /* Forward pass.
@@ -155,8 +155,10 @@ size_t attn_bwd_workspace_bytes(const attn_params* p);
  *   workspace: device memory of at least attn_bwd_workspace_bytes(p) bytes,
  *              16-byte aligned; its contents on entry do not matter.
  * The additive mask (p->mask, the same one the forward took), kv_lens,
- * causal and all three dtypes are supported (fp32 inputs take an all-fp32
- * path).  The result is deterministic: no atomics. */
+ * causal, the window, the grid and the soft cap (whose derivative
+ * 1 - tanh^2(s / softcap) multiplies dS) and all three dtypes are supported
+ * (fp32 inputs take an all-fp32 path).  The result is deterministic: no
+ * atomics. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,

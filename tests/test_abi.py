@@ -177,10 +177,11 @@ def test_local_and_softcap_validation():
     assert bd.attn_validate(_p(softcap=1e-44)) == inv                  # 2 scale log2e / cap overflows
     big = (1 << 28) + 10
     assert bd.attn_validate(_p(Nq=big, Nk=big, window_size=(8, 8))) == uns
-    # the backward does not take them
-    assert bd.attn_validate(_p(window_size=(16, 0)), True) == uns
-    assert bd.attn_validate(_p(grid=(8, 2, 2)), True) == uns
-    assert bd.attn_validate(_p(softcap=5.0), True) == uns
+    # the backward takes what the forward takes
+    assert bd.attn_validate(_p(window_size=(16, 0)), True) == ok
+    assert bd.attn_validate(_p(grid=(8, 2, 2), causal=True), True) == ok
+    assert bd.attn_validate(_p(softcap=5.0, dtype=bd.ATTN_FP32), True) == ok
+    assert bd.attn_validate(_p(window_size=(16, 0), Nk=65), True) == inv
 
 
 def test_decode_local_validation():

@@ -1,0 +1,167 @@
+"""GPU parity of the backward of local attention and the soft cap.
+
+attn_bwd with a sliding window, a 2-D neighbourhood and the tanh soft cap
+(alone and together, with causal, additive masks and key lengths), from the
+forward's own (O, LSE), against the fp64 oracle's exact backward
+(oracle.ref_bwd with the same options; the soft cap's derivative factor is
+pinned by central differences in tests/test_oracle_local.py).  The bars are
+those of tests/test_gpu_backward.py: max-abs 2e-2 for 16-bit inputs and
+1e-5 (relative to the gradient's scale) for fp32.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from exact_attention_25_amd import inputs
+from oracle import ref_bwd, ref_bwd_group
+from tests.gpu_util import from_layout, host, make_case, to_device, to_layout
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TOL_REL_RMS = 1e-2
+TOL_F32 = 1e-5
+REL_RMS_F32 = 3e-6
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _mask(B, Nq, Nk, seed):
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal((B, 1, Nq, Nk))
+    m[rng.random((B, 1, Nq, Nk)) < 0.05] = -np.inf
+    return m.astype(np.float32).astype(np.float64)
+
+
+def _run(w, x, layout, causal, mask, opts):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    t = {n: to_device(to_layout(x[n + "_raw"], layout), w.dtype) for n in ("q", "k", "v", "do")}
+    lens = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).cuda()
+    m = None if mask is None else torch.from_numpy(mask.astype(np.float32)).cuda()
+    kw = dict(layout=layout, causal=causal, attn_mask=m, kv_lens=lens,
+              window_size=opts.get("window", (-1, -1)), grid=opts.get("grid"),
+              softcap=opts.get("softcap", 0.0))
+    o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], **kw)
+    dq, dk, dv = bd.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], **kw)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check(name, got, ref, tol, rel):
+    g = host(got)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite"
+    err = np.abs(g - ref)
+    mx = float(err.max()) if err.size else 0.0
+    rr = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    rel_rms = float(np.sqrt(np.mean(err ** 2))) / rr if rr > 0 else 0.0
+    _say(f"  {name}: max-abs {mx:.2e} (bar {tol:.1e}), rel-rms {rel_rms:.2e}")
+    assert mx <= tol, f"{name}: max-abs {mx:.3e} > {tol}"
+    assert rel_rms <= rel, f"{name}: rel-rms {rel_rms:.3e}"
+    return mx
+
+
+CASES = [
+    # id, B, Hq, Hkv, N, d, dtype, layout, lens, qk_std (v, dO std 1), opts
+    ("bf16_window_gqa_lens", 2, 8, 2, 700, 128, "bf16", "bhnd", (300, 700), 1.0,
+     dict(window=(64, 0))),
+    ("fp16_window_both_sides_bnhd", 1, 4, 4, 513, 64, "fp16", "bnhd", None, 1.0,
+     dict(window=(100, 37))),
+    ("bf16_causal_window_d64", 1, 4, 1, 900, 64, "bf16", "bhnd", None, 1.0,
+     dict(window=(200, -1), causal=True)),
+    ("fp16_grid_causal_mask", 2, 2, 1, 200, 64, "fp16", "bhnd", None, 1.0,
+     dict(grid=(7, 2, 3), causal=True, mask=True)),
+    ("bf16_grid_56_r5_gqa16", 1, 16, 1, 640, 128, "bf16", "bhnd", None, 1.0,
+     dict(grid=(56, 5, 5))),
+    ("bf16_softcap_5_causal_gqa", 2, 8, 2, 640, 128, "bf16", "bhnd", (200, 640), 2.0,
+     dict(softcap=5.0, causal=True)),
+    ("fp16_softcap_30_bnhd", 1, 4, 4, 500, 64, "fp16", "bnhd", None, 2.5, dict(softcap=30.0)),
+    ("bf16_softcap_mask_d40", 1, 2, 2, 300, 40, "bf16", "bhnd", None, 2.0,
+     dict(softcap=3.0, mask=True)),
+    ("fp16_all_options", 2, 4, 2, 700, 128, "fp16", "bhnd", (350, 700), 2.0,
+     dict(window=(200, 90), grid=(25, 4, 6), softcap=4.0, mask=True)),
+    ("fp32_window_softcap", 1, 2, 1, 300, 64, "fp32", "bhnd", None, 1.5,
+     dict(window=(40, 10), softcap=5.0)),
+    ("fp32_grid_causal_lens", 1, 2, 2, 150, 128, "fp32", "bnhd", (90, 150), 1.0,
+     dict(grid=(12, 2, 3), causal=True)),
+    ("fp32_softcap_mask", 2, 2, 1, 200, 32, "fp32", "bhnd", None, 1.5,
+     dict(softcap=3.0, mask=True)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_local_backward(gpu_lib, case):
+    name, B, Hq, Hkv, N, d, dtype, layout, lens, std, opts = case
+    _say(f"[local-bwd] {name}")
+    opts = dict(opts)
+    seed = zlib.crc32(name.encode()) % 10000
+    w, x = make_case(B, Hq, Hkv, N, N, d, dtype, seed=seed, qk_std=std, lens=lens, with_do=True)
+    mask = _mask(B, N, N, seed) if opts.pop("mask", False) else None
+    causal = opts.pop("causal", False)
+    dq, dk, dv = _run(w, x, layout, causal, mask, opts)
+    dQ, dK, dV, _, _ = ref_bwd(x["q"], x["k"], x["v"], x["do"], causal=causal, mask=mask,
+                               kv_lens=x["kv_lens"], **opts)
+    for lbl, got, ref in (("dq", dq, dQ), ("dk", dk, dK), ("dv", dv, dV)):
+        if dtype == "fp32":
+            tol = TOL_F32 * max(1.0, float(np.abs(ref).max()))
+            _check(f"{name} {lbl}", from_layout(host(got), layout), ref, tol, REL_RMS_F32)
+        else:
+            _check(f"{name} {lbl}", from_layout(host(got), layout), ref, TOL, TOL_REL_RMS)
+
+
+def test_local_backward_rows_and_keys_without_pairs(gpu_lib):
+    """Batch 0 has no valid key; in batch 1 (150 keys) the window (10, 0)
+    leaves rows 160.. without a key and keys 150.. without a row: all of
+    their gradients are zero, the rest as the oracle."""
+    _say("[local-bwd] empty rows and keys")
+    w, x = make_case(2, 4, 2, 300, 300, 64, "bf16", seed=41, lens=(150, 150), with_do=True)
+    x["kv_lens"][0] = 0
+    dq, dk, dv = _run(w, x, "bhnd", False, None, dict(window=(10, 0)))
+    dQ, dK, dV, _, _ = ref_bwd(x["q"], x["k"], x["v"], x["do"], kv_lens=x["kv_lens"],
+                               window=(10, 0))
+    assert np.all(dQ[0] == 0) and np.all(dQ[1, :, 160:] == 0) and np.all(dK[1, :, 150:] == 0)
+    for lbl, got, ref in (("dq", dq, dQ), ("dk", dk, dK), ("dv", dv, dV)):
+        _check(lbl, got, ref, TOL, TOL_REL_RMS)
+    assert np.all(host(dq)[0] == 0) and np.all(host(dk)[1, :, 150:] == 0)
+
+
+def test_local_backward_open_equals_plain(gpu_lib):
+    """A window wider than the sequence gives the plain backward's gradients."""
+    _say("[local-bwd] open window equals plain")
+    w, x = make_case(1, 4, 2, 400, 400, 128, "bf16", seed=43, with_do=True)
+    g0 = _run(w, x, "bhnd", True, None, {})
+    g1 = _run(w, x, "bhnd", True, None, dict(window=(5000, 5000)))
+    for a, b in zip(g0, g1):
+        assert float((a - b).abs().max()) <= 5e-3
+
+
+def _workload_group(name, b, g):
+    """Full-size workload backward: one (batch, kv-head) group exactly."""
+    w = inputs.WORKLOADS[name]
+    _say(f"[local-bwd-workload] {name}: inputs")
+    x = inputs.make_inputs(w, with_do=True)
+    opts = {k: v for k, v in (("window", w.window), ("grid", w.grid),
+                              ("softcap", w.softcap or None)) if v}
+    _say(f"[local-bwd-workload] {name}: GPU forward + backward")
+    dq, dk, dv = _run(w, x, "bhnd", w.causal, None, opts)
+    G = w.Hq // w.Hkv
+    _say(f"[local-bwd-workload] {name}: oracle for batch {b}, kv-head {g}")
+    dQ, dK, dV, _, _ = ref_bwd_group(x["q"], x["k"], x["v"], x["do"], b, g, causal=w.causal,
+                                     kv_lens=x["kv_lens"], **opts)
+    _check("dq", dq[b, g * G:(g + 1) * G], dQ, TOL, TOL_REL_RMS)
+    _check("dk", dk[b, g], dK, TOL, TOL_REL_RMS)
+    _check("dv", dv[b, g], dV, TOL, TOL_REL_RMS)
+
+
+def test_workload_vit_softcap_backward(gpu_lib):
+    _workload_group("vit_softcap_bf16_b8_h12_n3136_d64", 7, 11)
+
+
+def test_workload_vit_neighbourhood_backward(gpu_lib):
+    _workload_group("vit_nbr_bf16_b8_h12_n3136_d64", 3, 5)
