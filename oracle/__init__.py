@@ -14,6 +14,9 @@ tiled_model
     A CPU model of the tiled double loop with an online softmax, following
     the steps the pages describe; used only to show that the recurrence
     reaches the plain definition.
+fp8_ref
+    FP8 (E4M3FN) codes, 64-row block quantisation with per-block scales, and
+    attention on the dequantised inputs.
 """
 from .attention_ref import (  # noqa: F401
     resolve_scale,
