@@ -172,7 +172,7 @@ def local_config(w) -> dict:
     return out
 
 
-def cpu_baseline(w, x, budget_s=15.0, backward=False, decode=False):
+def cpu_baseline(w, x, budget_s=15.0, backward=False, decode=False, fp8=False):
     """The fp64 oracle on (batch, head) pairs in order, until ~budget_s of CPU
     time; returns a dict in the metric's unit (TFLOP/s).  decode: the queries
     are the last positions of each batch's keys (the decode rule)."""
@@ -216,15 +216,25 @@ def cpu_baseline(w, x, budget_s=15.0, backward=False, decode=False):
                 per_head = acc.fwd_flops(1, 1, w.Nq, w.Nk, w.d, w.causal)
             for h in range(w.Hq):
                 g = h // G
-                ref_fwd(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, g:g + 1],
-                        x["v"][b:b + 1, g:g + 1], causal=w.causal, kv_lens=lens, **mods)
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                sk = (slice(b, b + 1), slice(g, g + 1))
+                if fp8:
+                    # the oracle's block quantisation and attention on the dequantised values
+                    from oracle.fp8_ref import quantize_blocks, ref_fwd_fp8
+                    (qc, qs), (kc, ks), (vc, vs) = (quantize_blocks(x[n][s]) for n, s in
+                                                    (("q", sl), ("k", sk), ("v", sk)))
+                    ref_fwd_fp8(qc, kc, vc, qs, ks, vs, causal=w.causal, kv_lens=lens)
+                else:
+                    ref_fwd(x["q"][sl], x["k"][sk], x["v"][sk], causal=w.causal, kv_lens=lens,
+                            **mods)
                 done += 1
                 flops += per_head
                 if time.perf_counter() - t0 >= budget_s:
                     break
             if time.perf_counter() - t0 >= budget_s:
                 break
-        what = "fp64 numpy oracle forward"
+        what = "fp64 numpy oracle FP8 forward (quantisation + attention)" if fp8 else \
+            "fp64 numpy oracle forward"
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
@@ -298,9 +308,10 @@ def main():
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch size (counter runs whose per-dispatch "
                          "cycle counts must stay below 2^31); the JSON line then names the new B")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode", "fp8"), default="fwd",
                     help="time the forward (default), the backward from the forward's O/LSE, "
-                         "or the split-KV decode (attn_decode; --workload a decode workload)")
+                         "the split-KV decode (attn_decode; --workload a decode workload), or "
+                         "the FP8 forward (attn_fwd_fp8 on attn_quantize_fp8's output)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the attention of every (batch, head) is "
@@ -346,7 +357,18 @@ def main():
     lkw = local_kw(w)
     fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"], **lkw)
     dec = args.which == "decode"
-    if dec:
+    fp8 = args.which == "fp8"
+    if fp8:
+        q8, k8, vt8, qs, ks, vs = bd.attn_quantize_fp8(t["q"], t["k"], t["v"])
+        qfn = lambda: bd.attn_quantize_fp8(t["q"], t["k"], t["v"])
+        q_ms, _ = time_calls(qfn, 10, 2, stream)
+        out_dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        o8 = torch.empty(t["q"].shape, dtype=out_dt, device=device)
+        l8 = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=device)
+        fn = lambda: bd.attn_fwd_fp8(q8, k8, vt8, qs, ks, vs, causal=w.causal, kv_lens=t["kv_lens"],
+                                     out_dtype=out_dt, out=o8, lse=l8)
+        flops = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    elif dec:
         dws = torch.empty(bd.attn_decode_workspace_bytes(bd.make_params(
             w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, bd.ATTN_BF16 if w.dtype == "bf16" else bd.ATTN_FP16,
             causal=w.causal, window_size=lkw["window_size"], softcap=w.softcap)),
@@ -377,7 +399,7 @@ def main():
     pct = call_percentiles(fn, min(args.steps, 50), stream)
 
     tflops = flops / ms / 1e9
-    peak = acc.PEAK_TFLOPS[w.dtype]
+    peak = acc.PEAK_TFLOPS["fp8" if fp8 else w.dtype]
     if dec:
         gbs = dec_bytes / ms / 1e6
         rec = {
@@ -418,7 +440,10 @@ def main():
         print(json.dumps(rec), flush=True)
         return
     metric = METRIC
-    if bwd and is_local(w):
+    if fp8:
+        metric = ("attention fwd FP8 TFLOPS (4*B*H*N^2*d; E4M3 operands with 64-row block scales) "
+                  "& % of the FP8 MFMA peak")
+    elif bwd and is_local(w):
         metric = "attention bwd TFLOPS (10*d FLOPs per visible (query, key) pair and head)"
     elif bwd:
         metric = "attention bwd TFLOPS (10*B*H*N^2*d, halved for causal)"
@@ -438,25 +463,30 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype})",
+        "dtype": "fp8_e4m3" if fp8 else w.dtype,
+        "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype}"
+                + (", then block-quantised to E4M3 by attn_quantize_fp8)" if fp8 else ")"),
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "Hkv": w.Hkv, "N": w.Nq,
                    "d": w.d, "causal": w.causal, "mask": None, "key_padding": w.lens is not None,
-                   "pass": "backward" if bwd else "forward", **local_config(w)},
+                   "pass": "fp8 forward" if fp8 else ("backward" if bwd else "forward"),
+                   **local_config(w)},
         "pct_of_peak": round(tflops / peak * 100, 2),
         "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": None if (bwd or w.name != DEFAULT_WORKLOAD) else recorded_traffic(),
+                     "traffic": None if (bwd or fp8 or w.name != DEFAULT_WORKLOAD) else recorded_traffic(),
                      "kernel": ("attn::bwd_prep_kernel + attn::bwd_q_kernel + attn::bwd_kv_kernel (+ reduce), one call per step"
-                                if bwd else fwd_kernel_name(w) + " (one launch per step)")},
+                                if bwd else ("attn::fwd_fp8_kernel (one launch per step)" if fp8
+                                             else fwd_kernel_name(w) + " (one launch per step)"))},
     }
+    if fp8:
+        rec["quantize_ms"] = round(q_ms, 4)
     if args.extras:
         print("[bench] extras", file=sys.stderr, flush=True)
         rec["extras"] = run_extras(device, max(args.steps // 5, 5), 3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, x, backward=bwd)
+        rec["cpu_baseline"] = cpu_baseline(w, x, backward=bwd, fp8=fp8)
     print(json.dumps(rec), flush=True)
 
 

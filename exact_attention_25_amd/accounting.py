@@ -17,7 +17,7 @@ from __future__ import annotations
 ELEM_BYTES = {"fp32": 4, "fp16": 2, "bf16": 2}
 
 # MI355X published peaks
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 
 

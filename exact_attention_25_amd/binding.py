@@ -19,7 +19,8 @@ ATTN_FP32, ATTN_FP16, ATTN_BF16 = 0, 1, 2
 ATTN_BHND, ATTN_BNHD = 0, 1
 
 EXPORTS = ("attn_validate", "attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_quantize_fp8", "attn_fwd_fp8",
+           "attn_status_string")
 
 
 class AttnParams(ctypes.Structure):
@@ -70,6 +71,10 @@ def load():
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_quantize_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_quantize_fp8.restype = ctypes.c_int
+    lib.attn_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_fwd_fp8.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -273,6 +278,76 @@ def attn_decode(q, k, v, *, layout="bhnd", causal=False, scale=None, kv_lens=Non
                          _stream_ptr(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+    return out, lse
+
+
+def _lens_arg(kv_lens, B):
+    torch = _torch()
+    if kv_lens is None:
+        return None, None
+    if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be an int32 device tensor with B entries")
+    kv_lens = kv_lens.contiguous()
+    return kv_lens, kv_lens.data_ptr()
+
+
+def attn_quantize_fp8(q, k, v, *, layout="bhnd"):
+    """FP8 (E4M3FN) block quantisation of q, k, v (64-row blocks, one fp32
+    scale per block).  Returns (q8, k8, vt8, q_scale, k_scale, v_scale):
+    q8 / k8 uint8 codes in q's / k's shape and layout, vt8 uint8
+    [B, Hkv, d, Nk rounded up to 64] (v transposed), scales float32
+    [B, H, ceil(N / 64)]."""
+    torch = _torch()
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
+    p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout))
+    dev = q.device
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    vt8 = torch.empty((B, Hkv, d, (Nk + 63) // 64 * 64), dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, Hq, (Nq + 63) // 64), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, Hkv, (Nk + 63) // 64), dtype=torch.float32, device=dev)
+    vs = torch.empty((B, Hkv, (Nk + 63) // 64), dtype=torch.float32, device=dev)
+    st = lib.attn_quantize_fp8(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs.data_ptr(),
+                               ks.data_ptr(), vs.data_ptr(), _stream_ptr(dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_quantize_fp8")
+    return q8, k8, vt8, qs, ks, vs
+
+
+def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, *, layout="bhnd", causal=False,
+                 scale=None, kv_lens=None, out_dtype=None, out=None, lse=None):
+    """FP8 forward on attn_quantize_fp8's outputs.  Returns (o, lse); o is
+    bf16 (default) or fp16 in q's shape and layout."""
+    torch = _torch()
+    lib = load()
+    if q8.dim() != 4 or k8.dim() != 4 or q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise ValueError("q8, k8 must be 4-D uint8 tensors")
+    if layout == "bhnd":
+        B, Hq, Nq, d = q8.shape
+        _, Hkv, Nk, _ = k8.shape
+    else:
+        B, Nq, Hq, d = q8.shape
+        _, Nk, Hkv, _ = k8.shape
+    if tuple(vt8.shape) != (B, Hkv, d, (Nk + 63) // 64 * 64):
+        raise ValueError("vt8 must be [B, Hkv, d, Nk rounded up to 64]")
+    for t in (q8, k8, vt8, q_scale, k_scale, v_scale):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("fp8 inputs must be contiguous device tensors")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    kv_lens, lens_ptr = _lens_arg(kv_lens, B)
+    p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(out_dtype), _layout_code(layout), scale,
+                    causal, None, (0, 0, 0), lens_ptr)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=out_dtype, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+    st = lib.attn_fwd_fp8(ctypes.byref(p), q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(),
+                          q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), _stream_ptr(q8.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8")
     return out, lse
 
 

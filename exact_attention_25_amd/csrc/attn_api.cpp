@@ -350,6 +350,99 @@ attn_status attn_decode(const attn_params* p, const void* q, const void* k, cons
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+attn_status validate_fp8(const attn_params* p) {
+  if (!p) return ATTN_EINVAL;
+  const attn_status st = attn_validate(p, 0);
+  if (st != ATTN_OK) return st;
+  if (p->d % 16 != 0) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_quantize_fp8(const attn_params* p, const void* q, const void* k, const void* v,
+                              void* q8, void* k8, void* vt8, float* q_scale, float* k_scale,
+                              float* v_scale, void* stream) {
+  const attn_status st = validate_fp8(p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0) return ATTN_OK;
+  const bool has_q = p->Nq > 0, has_k = p->Nk > 0;
+  if ((has_q && (!q || !q8 || !q_scale)) || (has_k && (!k || !v || !k8 || !vt8 || !k_scale || !v_scale)))
+    return ATTN_EINVAL;
+  const void* ptrs[] = {q, k, v, q8, k8, vt8, q_scale, k_scale, v_scale};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return ATTN_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int in_dtype = p->dtype == ATTN_BF16 ? 2 : (p->dtype == ATTN_FP16 ? 1 : 0);
+  auto one = [&](const void* x, void* out, float* scale, int H, int N, bool transpose) {
+    attn::QuantArgs a = {};
+    const Strides sx = strides_for(p->layout, H, N, p->d);
+    a.x = x;
+    a.out = out;
+    a.scale = scale;
+    a.x_sb = sx.sb; a.x_sh = sx.sh; a.x_sn = sx.sn;
+    a.o_sb = sx.sb; a.o_sh = sx.sh; a.o_sn = sx.sn;   // 1-byte codes: same numbers
+    a.o_ld = round64(N);
+    a.B = p->B; a.H = H; a.N = N; a.d = p->d;
+    a.nblk = (N + 63) / 64;
+    a.transpose = transpose ? 1 : 0;
+    return attn::launch_fp8_quant(a, in_dtype, s);
+  };
+  hipError_t e = hipSuccess;
+  if (has_q) e = one(q, q8, q_scale, p->Hq, p->Nq, false);
+  if (e == hipSuccess && has_k) e = one(k, k8, k_scale, p->Hkv, p->Nk, false);
+  if (e == hipSuccess && has_k) e = one(v, vt8, v_scale, p->Hkv, p->Nk, true);
+  return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+attn_status attn_fwd_fp8(const attn_params* p, const void* q8, const void* k8, const void* vt8,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         void* o, float* lse, void* stream) {
+  const attn_status st = validate_fp8(p);
+  if (st != ATTN_OK) return st;
+  if (p->dtype == ATTN_FP32 || p->mask || is_local(p) || p->softcap > 0.0f)
+    return ATTN_EUNSUPPORTED;
+  if (p->B == 0 || p->Nq == 0) return ATTN_OK;
+  if (!q8 || !q_scale || !o || !lse) return ATTN_EINVAL;
+  if (p->Nk > 0 && (!k8 || !vt8 || !k_scale || !v_scale)) return ATTN_EINVAL;
+  const void* ptrs[] = {q8, k8, vt8, q_scale, k_scale, v_scale, o, lse};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return ATTN_EALIGN;
+  if (p->kv_lens && (reinterpret_cast<uintptr_t>(p->kv_lens) & 3u)) return ATTN_EALIGN;
+  attn::Fp8Args a = {};
+  a.q = static_cast<const uint8_t*>(q8);
+  a.k = static_cast<const uint8_t*>(k8);
+  a.vt = static_cast<const uint8_t*>(vt8);
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.o = o;
+  a.lse = lse;
+  a.kv_lens = p->kv_lens;
+  const Strides sq = strides_for(p->layout, p->Hq, p->Nq, p->d);
+  const Strides sk = strides_for(p->layout, p->Hkv, p->Nk, p->d);
+  a.q_sb = sq.sb; a.q_sh = sq.sh; a.q_sn = sq.sn;
+  a.o_sb = sq.sb; a.o_sh = sq.sh; a.o_sn = sq.sn;
+  a.k_sb = sk.sb; a.k_sh = sk.sh; a.k_sn = sk.sn;
+  a.vt_ld = round64(p->Nk);
+  a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.d = p->d;
+  a.group = p->Hq / p->Hkv;
+  a.nqs = (p->Nq + 63) / 64;
+  a.nks = (p->Nk + 63) / 64;
+  a.c = resolve_scale(p) * kLog2eF;
+  const hipError_t e = attn::launch_fwd_fp8(a, p->dtype == ATTN_BF16, p->causal != 0,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
 const char* attn_status_string(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ok";

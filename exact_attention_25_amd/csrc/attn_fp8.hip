@@ -1,0 +1,392 @@
+// FP8 attention forward for gfx950 with per-block scales, and the block
+// quantiser that produces its inputs.
+//
+// The pages' FP8 variant ("FlashAttention技术解析：优化Transformer注意力计算效率"
+// (jsqmd.com/news/722897) §4.2 item 3 and §6.3 item 2): block quantisation,
+// both matrix products on FP8 operands, an independent scale per block, the
+// softmax statistics in fp32.  Here:
+//   - format OCP E4M3FN (the conversion instructions' format on gfx950);
+//   - blocks of 64 rows of one (batch, head): scale = amax / 448, so a block's
+//     largest magnitude maps to 448;
+//   - V is stored transposed ([B, Hkv, d, Nk rounded up to 64], keys
+//     contiguous), so the operand of the PV product is read as plain rows;
+//   - the products run on v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 per
+//     instruction, unit hardware scales); the fp32 block scales are folded
+//     into the exponent: s -> s * scale * sq * sk * log2(e) per (wave, tile).
+//
+// Forward, per (batch, q-head, 256 query rows); 8 waves of 32 rows; 64-key
+// tiles of K (row-major) and V^T through double-buffered LDS filled by
+// direct buffer->LDS loads.  Per tile and wave:
+//   S^T = K Q^T    A = K rows read in a permuted order, B = Q^T from
+//                  registers.  The MFMA contracts slot i of lane half h of A
+//                  with slot i of lane half h of B, and its result puts row
+//                  8 (r / 4) + 4 h + r % 4 in register r; reading key
+//                  32 ((i / 4) % 2) + 16 blk + 4 (i / 8) + i % 4 for row i
+//                  of 32-key block blk makes register r of lane half h hold
+//                  key 32 h + 16 blk + r, so a lane half holds 32
+//                  consecutive keys.
+//   softmax        p = exp2(s c sq sk - m + log2(sv / svmax) + 7), with the
+//                  reference m moved lazily by more than 1 (so p <= 256 <
+//                  448); the V block scale sv enters through p (relative to
+//                  the head's largest svmax) and the factor 2^7 keeps small
+//                  p out of E4M3's subnormal range; l sums p in fp32;
+//   O^T += V^T P^T  P packed to E4M3 (slot 16 blk + r = key 32 h + 16 blk + r)
+//                  as the B operand; A = 32 consecutive keys of a V^T row.
+// Epilogue: O = acc * svmax * 2^-7 / l, LSE = ln2 (m + log2 l).
+#include "attn_kernels.h"
+#include "device_common.h"
+
+namespace attn {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // unit E8M0 scales (127) for both operands
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// E4M3 codes of four floats (nearest even) in one word, a in the low byte.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
+
+// ------------------------------------------------------------- quantiser
+// One work-group of 256 threads per (batch, head, block of 64 rows): the
+// block's amax, scale = amax / 448 and codes of x * (448 / amax), both
+// divisions and the product in fp32 (a zero block gets scale 1 and zero
+// codes).  transpose: the codes go to [B, H, d, ld] with keys contiguous,
+// and the block writes all 64 of its columns (zeros past N).
+template <class T>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs a) {
+  __shared__ float red[4];
+  __shared__ float sc[2];
+  const int tid = threadIdx.x;
+  int w = blockIdx.x;
+  const int blk = w % a.nblk;
+  w /= a.nblk;
+  const int h = w % a.H, b = w / a.H;
+  const int r0 = blk * 64;
+  const int rows = min(64, a.N - r0);
+  const T* x = (const T*)a.x + b * a.x_sb + h * a.x_sh + (int64_t)r0 * a.x_sn;
+
+  float amax = 0.f;
+  for (int e = tid; e < rows * a.d; e += 256) {
+    const int r = e / a.d, c = e - r * a.d;
+    amax = fmaxf(amax, fabsf((float)x[r * a.x_sn + c]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  if (tid == 0) {
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    sc[0] = m > 0.f ? m / 448.0f : 1.0f;
+    sc[1] = m > 0.f ? 448.0f / m : 1.0f;
+    a.scale[((int64_t)b * a.H + h) * a.nblk + blk] = sc[0];
+  }
+  __syncthreads();
+  const float inv = sc[1];
+  if (!a.transpose) {
+    uint8_t* o = (uint8_t*)a.out + b * a.o_sb + h * a.o_sh + (int64_t)r0 * a.o_sn;
+    const int q4 = a.d / 4;
+    for (int e = tid; e < rows * q4; e += 256) {
+      const int r = e / q4, c = (e - r * q4) * 4;
+      const T* p = x + r * a.x_sn + c;
+      const int v = pack_fp8x4((float)p[0] * inv, (float)p[1] * inv, (float)p[2] * inv,
+                               (float)p[3] * inv);
+      *(int*)(o + r * a.o_sn + c) = v;
+    }
+  } else {
+    // column c of the block: keys r0 .. r0+63 at o + c * ld + r0
+    uint8_t* o = (uint8_t*)a.out + ((int64_t)b * a.H + h) * a.d * a.o_ld + r0;
+    for (int e = tid; e < a.d * 16; e += 256) {
+      const int c = e >> 4, j = (e & 15) * 4;
+      float f[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = j + i < rows ? (float)x[(j + i) * a.x_sn + c] * inv : 0.f;
+      *(int*)(o + (int64_t)c * a.o_ld + j) = pack_fp8x4(f[0], f[1], f[2], f[3]);
+    }
+  }
+}
+
+hipError_t launch_fp8_quant(const QuantArgs& a, int in_dtype, hipStream_t st) {
+  const long n = (long)a.B * a.H * a.nblk;
+  if (n == 0) return hipSuccess;
+  if (in_dtype == 2)
+    hipLaunchKernelGGL(fp8_quant_kernel<__bf16>, dim3((unsigned)n), dim3(256), 0, st, a);
+  else if (in_dtype == 1)
+    hipLaunchKernelGGL(fp8_quant_kernel<_Float16>, dim3((unsigned)n), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(fp8_quant_kernel<float>, dim3((unsigned)n), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- forward
+template <class E, int D, bool CAUSAL>
+struct Fp8Fwd {
+  static constexpr int NW = 8, ROWS = NW * 32, BC = 64;
+  static constexpr int KS = D / 64;                    // K = 64 steps of QK^T
+  static constexpr int DT = D / 32;                    // 32-row blocks of O^T
+  static constexpr int KPS = D / 16 + 1;               // K row: D bytes + one pad slot
+  static constexpr int VPS = BC / 16 + 1;              // V^T row: 64 bytes + one pad slot
+  static constexpr int KP = KPS * 16, VP = VPS * 16;
+  static constexpr int K_BYTES = BC * KP, V_BYTES = D * VP;
+  static constexpr int K_INS = (BC * KPS + 63) / 64, V_INS = (D * VPS + 63) / 64;
+  static constexpr int K_IPW = (K_INS + NW - 1) / NW, V_IPW = (V_INS + NW - 1) / NW;
+  static constexpr float TH = 1.0f;                    // lazy rescale threshold (log2)
+  using T = typename E::T;
+  using V4 = typename E::V4;
+
+  struct State {
+    int lane, wave, hl, l32;
+    int q_w0, kv_limit, n_act;
+    const uint8_t* kp;          // K of this (batch, kv-head), key 0
+    const uint8_t* vp;          // V^T of this (batch, kv-head), column 0
+    const float* ksc;           // K / V block scales of this (batch, kv-head)
+    const float* vsc;
+    int64_t k_tile, k_end;
+    uint32_t koff[K_IPW], voff[V_IPW];
+    int kbase, vbase;
+    float cq;                   // scale * log2(e) * sq
+    float lsv_max;              // log2 of the head's largest V block scale
+    i32x8 qf[KS];
+    f32x16 acc[DT];
+    float m_run, l_run;
+  };
+
+  static __device__ __forceinline__ void issue(const Fp8Args& a, const State& st, int j,
+                                               char* kb, char* vb) {
+    const int64_t ko = (int64_t)j * st.k_tile;
+    const BufRsrc rk = make_rsrc(st.kp + ko, (uint32_t)min(st.k_end - ko, (int64_t)kBufLimit));
+    const BufRsrc rv = make_rsrc(st.vp + (int64_t)j * BC, (uint32_t)kBufLimit);
+#pragma unroll
+    for (int i = 0; i < K_IPW; ++i) {
+      const int ins = i * NW + st.wave;
+      if (ins < K_INS) dma16_buf(rk, st.koff[i], kb + ins * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < V_IPW; ++i) {
+      const int ins = i * NW + st.wave;
+      if (ins < V_INS) dma16_buf(rv, st.voff[i], vb + ins * 1024);
+    }
+  }
+
+  static __device__ __forceinline__ i32x8 read32(const char* p) {
+    const i32x4 lo = lds_read16<i32x4>(p), hi = lds_read16<i32x4>(p + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+
+  static __device__ __forceinline__ void tile(const Fp8Args& a, State& st, const char* kb,
+                                              const char* vb, int j) {
+    const int j0 = j * BC;
+    // S^T of the tile's two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[blk] = mfma_fp8(read32(kb + st.kbase + blk * 16 * KP + ks * 64), st.qf[ks], s[blk]);
+    }
+    // register r of block blk: key j0 + 32 hl + 16 blk + r
+    const int qrow = st.q_w0 + st.l32;
+    const bool edge = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
+    if (edge) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * st.hl + 16 * blk + r;
+          if (key >= st.kv_limit || (CAUSAL && key > qrow)) s[blk][r] = -INFINITY;
+        }
+    }
+    const float cs = st.cq * st.ksc[j];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+    mx = max_with_other_half(mx) * cs;
+    if (__builtin_amdgcn_ballot_w64(mx > st.m_run + TH)) {
+      const float m_new = fmaxf(st.m_run, mx);
+      if (m_new > st.m_run) {
+        const float alpha = (st.m_run == -INFINITY) ? 0.f : fast_exp2(st.m_run - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+        st.m_run = m_new;
+      }
+    }
+    const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
+    // p' = p sv / svmax 2^7 = exp2(s cs - mref + log2(sv) - log2(svmax) + 7)
+    const float lr = fast_log2(st.vsc[j]) - st.lsv_max + 7.0f;
+    const float off = lr - mref;
+    float psum = 0.f;
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int blk = w >> 2, r = (w & 3) * 4;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(__builtin_fmaf(s[blk][r + i], cs, off));
+        psum += p[i];
+      }
+      pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+    }
+    // l in units of p: divide the tile's sum by 2^lr
+    st.l_run = __builtin_fmaf(psum, fast_exp2(-lr), st.l_run);
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      st.acc[dt] = mfma_fp8(read32(vb + st.vbase + dt * 32 * VP), pf, st.acc[dt]);
+  }
+
+  static __device__ __forceinline__ void step(const Fp8Args& a, State& st, int j, int n,
+                                              const char* kc, const char* vc, char* kn,
+                                              char* vn) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < n) issue(a, st, j + 1, kn, vn);
+    if (j < st.n_act) tile(a, st, kc, vc, j);
+  }
+
+  static __device__ __forceinline__ void run(const Fp8Args& a, char* k0, char* v0, char* k1,
+                                             char* v1) {
+    State st;
+    st.lane = threadIdx.x & 63;
+    st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    st.hl = st.lane >> 5;
+    st.l32 = st.lane & 31;
+
+    const int wid = xcd_remap(blockIdx.x, a.total_blocks);
+    int qblk = wid % a.nqb;
+    const int bh = wid / a.nqb;
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    if (CAUSAL) qblk = a.nqb - 1 - qblk;   // longest rows first
+    const int g = h / a.group;
+    const int q_blk0 = qblk * ROWS;
+    st.q_w0 = q_blk0 + st.wave * 32;
+
+    st.kv_limit = a.Nk;
+    if (a.kv_lens) st.kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
+    int kv_end = st.kv_limit;
+    if (CAUSAL) kv_end = min(kv_end, min(q_blk0 + ROWS, a.Nq));
+    const int n_tiles = (kv_end + BC - 1) / BC;
+    st.n_act = CAUSAL ? min(n_tiles, (st.q_w0 + 31) / BC + 1) : n_tiles;
+
+    st.kp = a.k + b * a.k_sb + g * a.k_sh;
+    st.vp = a.vt + ((int64_t)b * a.Hkv + g) * a.d * a.vt_ld;
+    st.ksc = a.k_scale + ((int64_t)b * a.Hkv + g) * a.nks;
+    st.vsc = a.v_scale + ((int64_t)b * a.Hkv + g) * a.nks;
+    st.k_tile = (int64_t)BC * a.k_sn;
+    st.k_end = (int64_t)(a.Nk - 1) * a.k_sn + a.d;
+    const int dch = a.d / 16;
+    // K tile: slot s = row s / KPS, chunk s % KPS (pad slot and chunks past d
+    // load zero); V^T tile: row (d index) s / VPS, chunk s % VPS of 64 keys
+#pragma unroll
+    for (int i = 0; i < K_IPW; ++i) {
+      const int s = (i * NW + st.wave) * 64 + st.lane;
+      const int r = s / KPS, ch = s % KPS;
+      st.koff[i] = (r < BC && ch < dch) ? (uint32_t)(r * a.k_sn + ch * 16) : kBufOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < V_IPW; ++i) {
+      const int s = (i * NW + st.wave) * 64 + st.lane;
+      const int r = s / VPS, ch = s % VPS;
+      st.voff[i] = (r < a.d && ch < BC / 16) ? (uint32_t)(r * a.vt_ld + ch * 16) : kBufOutOfRange;
+    }
+    {
+      // K row of S^T row l32 in 32-key block 0 (block 1 adds 16 rows)
+      const int i = st.l32;
+      const int key = 32 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+      st.kbase = key * KP + st.hl * 32;
+      st.vbase = st.l32 * VP + st.hl * 32;
+    }
+
+    // Q^T operand: 32 bytes of row q_w0 + l32 per K = 64 step (zero past d)
+    const int crow = min(st.q_w0 + st.l32, a.Nq - 1);
+    const uint8_t* qp = a.q + b * a.q_sb + h * a.q_sh + (int64_t)crow * a.q_sn;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = ks * 64 + st.hl * 32;
+      const i32x4 lo = d0 < a.d ? *(const i32x4*)(qp + d0) : i32x4{};
+      const i32x4 hi = d0 + 16 < a.d ? *(const i32x4*)(qp + d0 + 16) : i32x4{};
+      st.qf[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const float sq = a.q_scale[((int64_t)b * a.Hq + h) * a.nqs + min(st.q_w0, a.Nq - 1) / 64];
+    st.cq = a.c * sq;
+    // the head's largest V block scale over the tiles this block reads
+    float svm = 0.f;
+    for (int t = st.lane; t < n_tiles; t += 64) svm = fmaxf(svm, st.vsc[t]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) svm = fmaxf(svm, __shfl_xor(svm, o, 64));
+    st.lsv_max = svm > 0.f ? fast_log2(svm) : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    if (n_tiles > 0) issue(a, st, 0, k0, v0);
+    for (int j = 0; j < n_tiles; j += 2) {
+      step(a, st, j, n_tiles, k0, v0, k1, v1);
+      if (j + 1 >= n_tiles) break;
+      step(a, st, j + 1, n_tiles, k1, v1, k0, v0);
+    }
+
+    T* op = (T*)a.o + b * a.o_sb + h * a.o_sh;
+    const float l_tot = add_with_other_half(st.l_run);
+    const float inv = l_tot > 0.f ? svm * 0.0078125f / l_tot : 0.f;   // svmax 2^-7 / l
+    const int row = st.q_w0 + st.l32;
+    if (row < a.Nq) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = dt * 32 + gq * 8 + st.hl * 4;
+          if (col < a.d) {
+            auto lo = E::cvt2(st.acc[dt][gq * 4 + 0] * inv, st.acc[dt][gq * 4 + 1] * inv);
+            auto hi = E::cvt2(st.acc[dt][gq * 4 + 2] * inv, st.acc[dt][gq * 4 + 3] * inv);
+            *(V4*)(op + row * a.o_sn + col) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+          }
+        }
+      if (st.hl == 0)
+        a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] =
+            l_tot > 0.f ? (st.m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+};
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_fp8_kernel(Fp8Args a) {
+  using K = Fp8Fwd<E, D, CAUSAL>;
+  __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[K::V_BYTES];
+  K::run(a, k0, v0, k1, v1);
+}
+
+template <class E, int D>
+static hipError_t launch_fp8_d(const Fp8Args& a0, bool causal, hipStream_t st) {
+  Fp8Args a = a0;
+  a.nqb = (a.Nq + 255) / 256;
+  a.total_blocks = a.B * a.Hq * a.nqb;
+  if (a.total_blocks == 0) return hipSuccess;
+  if (causal)
+    hipLaunchKernelGGL((fwd_fp8_kernel<E, D, true>), dim3(a.total_blocks), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<E, D, false>), dim3(a.total_blocks), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, bool out_bf16, bool causal, hipStream_t st) {
+  if (a.d > 64)
+    return out_bf16 ? launch_fp8_d<BF16, 128>(a, causal, st) : launch_fp8_d<FP16, 128>(a, causal, st);
+  return out_bf16 ? launch_fp8_d<BF16, 64>(a, causal, st) : launch_fp8_d<FP16, 64>(a, causal, st);
+}
+
+}  // namespace attn

@@ -99,6 +99,48 @@ struct DecodeArgs {
   float cap_a, cap_c2;   // soft cap (see FwdArgs), used when soft-capped
 };
 
+// Kernel arguments of the FP8 forward (attn_fp8.hip).  q, k hold E4M3 codes
+// in the layout of the call (strides in elements = bytes); vt holds V
+// transposed, [B, Hkv, d, vt_ld] with keys contiguous; every scale array
+// has one fp32 value per 64 rows of a (batch, head).
+struct Fp8Args {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* vt;
+  const float* q_scale;  // [B, Hq, nqs]
+  const float* k_scale;  // [B, Hkv, nks]
+  const float* v_scale;  // [B, Hkv, nks]
+  void* o;
+  float* lse;
+  const int32_t* kv_lens;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t vt_ld;         // Nk rounded up to 64
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t group;
+  int32_t nqs, nks;      // 64-row blocks per head of q and of k / v
+  int32_t nqb, total_blocks;  // set by the launcher
+  float c;               // scale * log2(e)
+};
+
+// Kernel arguments of the FP8 block quantiser: x [B, H, N, d] in a layout
+// (element strides) -> codes (natural: byte strides o_*; transposed:
+// [B, H, d, o_ld]) and one scale per 64 rows.
+struct QuantArgs {
+  const void* x;
+  void* out;
+  float* scale;          // [B, H, nblk]
+  int64_t x_sb, x_sh, x_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t o_ld;
+  int32_t B, H, N, d, nblk;
+  int32_t transpose;
+};
+
+hipError_t launch_fp8_quant(const QuantArgs& a, int in_dtype, hipStream_t st);
+hipError_t launch_fwd_fp8(const Fp8Args& a, bool out_bf16, bool causal, hipStream_t st);
+
 // Split of the decode's keys, shared by the workspace sizing and the launch.
 void decode_split(int B, int Hkv, int rows, int Nk, int* split_keys, int* n_splits);
 hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, bool softcap, hipStream_t st);

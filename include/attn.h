@@ -191,6 +191,39 @@ attn_status attn_decode(const attn_params* p, const void* q, const void* k,
                         const void* v, void* o, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* FP8 block quantisation for attn_fwd_fp8 (the FP8 variant of
+ * "FlashAttention技术解析：优化Transformer注意力计算效率" (jsqmd.com/news/722897)
+ * §4.2 item 3 and §6.3 item 2: FP8 matrix operands, one scale per block).
+ * Every 64 consecutive rows of one (batch, head) of q, k and v form a block
+ * with scale s = amax / 448 (1 for an all-zero block), computed in fp32, and
+ * each element becomes the OCP FP8 E4M3FN code of fp32(x * (448 / amax)),
+ * rounded to nearest even; the value a code stands for is code * s.
+ *   q, k, v:  as for attn_fwd, element type p->dtype (any of the three)
+ *   q8, k8:   outputs, E4M3 codes, q's and k's shape and layout (1 byte each)
+ *   vt8:      output, v's codes transposed: [B, Hkv, d, ldv] bytes with
+ *             ldv = Nk rounded up to 64 (keys contiguous; columns past Nk 0)
+ *   q_scale:  output, [B, Hq, ceil(Nq / 64)] float
+ *   k_scale, v_scale: outputs, [B, Hkv, ceil(Nk / 64)] float
+ * Needs d % 16 == 0 (ATTN_EUNSUPPORTED otherwise); every pointer 16-byte
+ * aligned.  p's mask, window, grid and soft cap are ignored. */
+attn_status attn_quantize_fp8(const attn_params* p, const void* q, const void* k,
+                              const void* v, void* q8, void* k8, void* vt8, float* q_scale,
+                              float* k_scale, float* v_scale, void* stream);
+
+/* FP8 forward on the outputs of attn_quantize_fp8: the same O and LSE as
+ * attn_fwd on the dequantised inputs (code * block scale), with both matrix
+ * products on FP8 operands: the probabilities are rounded to E4M3 for the
+ * product with V (relative error up to 2^-4 per probability), the softmax
+ * statistics stay fp32.
+ *   p->dtype: the element type of o (ATTN_BF16 or ATTN_FP16); p->layout: the
+ *   layout of q8, k8 and o; causal, kv_lens, GQA and scale as for attn_fwd.
+ *   o: output, q's shape and layout; lse: output, [B, Hq, Nq] float.
+ * ATTN_EUNSUPPORTED for an fp32 output, an additive mask, a window, a grid,
+ * a soft cap or d % 16 != 0. */
+attn_status attn_fwd_fp8(const attn_params* p, const void* q8, const void* k8,
+                         const void* vt8, const float* q_scale, const float* k_scale,
+                         const float* v_scale, void* o, float* lse, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status s);
 

@@ -195,3 +195,28 @@ def test_decode_local_validation():
     full = ws(bd.make_params(**dict(base, Nk=65536), causal=True))
     win = ws(bd.make_params(**dict(base, Nk=65536), causal=True, window_size=(1023, 0)))
     assert 0 < win < full
+
+
+def test_fp8_validation_and_errors():
+    import ctypes as ct
+    lib = bd.load()
+    nul = None
+
+    def fwd(**kw):
+        p = _p(**kw)
+        return lib.attn_fwd_fp8(ct.byref(p), nul, nul, nul, nul, nul, nul, nul, nul, nul)
+
+    def quant(**kw):
+        p = _p(**kw)
+        return lib.attn_quantize_fp8(ct.byref(p), nul, nul, nul, nul, nul, nul, nul, nul, nul,
+                                     nul)
+
+    assert fwd(d=40) == bd.ATTN_EUNSUPPORTED                      # d % 16
+    assert quant(d=40) == bd.ATTN_EUNSUPPORTED
+    assert fwd(dtype=bd.ATTN_FP32) == bd.ATTN_EUNSUPPORTED        # fp32 output
+    assert fwd(softcap=2.0) == bd.ATTN_EUNSUPPORTED
+    assert fwd(window_size=(8, 0)) == bd.ATTN_EUNSUPPORTED
+    assert fwd(Hq=6, Hkv=4) == bd.ATTN_EINVAL
+    assert fwd() == bd.ATTN_EINVAL                                # null pointers
+    assert quant() == bd.ATTN_EINVAL
+    assert fwd(B=0) == bd.ATTN_OK and quant(B=0) == bd.ATTN_OK
