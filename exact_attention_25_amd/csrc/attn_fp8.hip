@@ -29,10 +29,15 @@
 //                  reference m moved lazily by more than 1 (so p <= 256 <
 //                  448); the V block scale sv enters through p (relative to
 //                  the head's largest svmax) and the factor 2^7 keeps small
-//                  p out of E4M3's subnormal range; l sums p in fp32;
+//                  p out of E4M3's subnormal range;
 //   O^T += V^T P^T  P packed to E4M3 (slot 16 blk + r = key 32 h + 16 blk + r)
-//                  as the B operand; A = 32 consecutive keys of a V^T row.
-// Epilogue: O = acc * svmax * 2^-7 / l, LSE = ln2 (m + log2 l).
+//                  as the B operand; A = 32 consecutive keys of a V^T row;
+//   sums           one more MFMA with all-ones codes as A sums the rounded
+//                  P over the tile's keys (every row of its result holds
+//                  the column sums), the divisor of O; an fp32 sum of the
+//                  unrounded p gives the LSE.
+// The block scales of tile j+1 are loaded before the barrier of tile j.
+// Epilogue: O = acc * svmax * 2^-7 / l_rounded, LSE = ln2 (m + log2 l).
 #include "attn_kernels.h"
 #include "device_common.h"
 
@@ -53,15 +58,20 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 }
 
 // ------------------------------------------------------------- quantiser
-// One work-group of 256 threads per (batch, head, block of 64 rows): the
-// block's amax, scale = amax / 448 and codes of x * (448 / amax), both
-// divisions and the product in fp32 (a zero block gets scale 1 and zero
-// codes).  transpose: the codes go to [B, H, d, ld] with keys contiguous,
-// and the block writes all 64 of its columns (zeros past N).
+// One work-group of 256 threads per (batch, head, block of 64 rows).  The
+// block is read once, in 16-byte chunks kept in registers: amax, then
+// scale = amax / 448 and the codes of x * (448 / amax), both divisions and
+// the product in fp32 (a zero block gets scale 1 and zero codes).  Natural
+// layout: each chunk's codes are stored at once.  transpose: the codes go
+// through an LDS tile to [B, H, d, ld] with keys contiguous, and the block
+// writes all 64 of its columns (zeros past N).
 template <class T>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs a) {
+  constexpr int CH = 16 / sizeof(T);                  // elements per 16-byte chunk
+  constexpr int MAXC = 64 * 128 / CH / 256;           // chunks per thread (d <= 128)
   __shared__ float red[4];
   __shared__ float sc[2];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * 128];   // transposed path
   const int tid = threadIdx.x;
   int w = blockIdx.x;
   const int blk = w % a.nblk;
@@ -69,12 +79,21 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs a) {
   const int h = w % a.H, b = w / a.H;
   const int r0 = blk * 64;
   const int rows = min(64, a.N - r0);
+  const int cpr = a.d / CH;                           // chunks per row
   const T* x = (const T*)a.x + b * a.x_sb + h * a.x_sh + (int64_t)r0 * a.x_sn;
 
+  typedef T TV __attribute__((ext_vector_type(CH)));
+  TV v[MAXC];
   float amax = 0.f;
-  for (int e = tid; e < rows * a.d; e += 256) {
-    const int r = e / a.d, c = e - r * a.d;
-    amax = fmaxf(amax, fabsf((float)x[r * a.x_sn + c]));
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + i * 256;
+    if (c < rows * cpr) {
+      const int r = c / cpr, ch = c - r * cpr;
+      v[i] = *(const TV*)(x + r * a.x_sn + ch * CH);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) amax = fmaxf(amax, fabsf((float)v[i][e]));
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
@@ -88,26 +107,34 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantArgs a) {
   }
   __syncthreads();
   const float inv = sc[1];
-  if (!a.transpose) {
-    uint8_t* o = (uint8_t*)a.out + b * a.o_sb + h * a.o_sh + (int64_t)r0 * a.o_sn;
-    const int q4 = a.d / 4;
-    for (int e = tid; e < rows * q4; e += 256) {
-      const int r = e / q4, c = (e - r * q4) * 4;
-      const T* p = x + r * a.x_sn + c;
-      const int v = pack_fp8x4((float)p[0] * inv, (float)p[1] * inv, (float)p[2] * inv,
-                               (float)p[3] * inv);
-      *(int*)(o + r * a.o_sn + c) = v;
-    }
-  } else {
-    // column c of the block: keys r0 .. r0+63 at o + c * ld + r0
-    uint8_t* o = (uint8_t*)a.out + ((int64_t)b * a.H + h) * a.d * a.o_ld + r0;
-    for (int e = tid; e < a.d * 16; e += 256) {
-      const int c = e >> 4, j = (e & 15) * 4;
-      float f[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = j + i < rows ? (float)x[(j + i) * a.x_sn + c] * inv : 0.f;
-      *(int*)(o + (int64_t)c * a.o_ld + j) = pack_fp8x4(f[0], f[1], f[2], f[3]);
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + i * 256;
+    if (c < rows * cpr) {
+      const int r = c / cpr, ch = c - r * cpr;
+      int wds[CH / 4];
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q)
+        wds[q] = pack_fp8x4((float)v[i][4 * q] * inv, (float)v[i][4 * q + 1] * inv,
+                            (float)v[i][4 * q + 2] * inv, (float)v[i][4 * q + 3] * inv);
+      uint8_t* dst = a.transpose ? tile + r * a.d + ch * CH
+                                 : (uint8_t*)a.out + b * a.o_sb + h * a.o_sh +
+                                       (int64_t)(r0 + r) * a.o_sn + ch * CH;
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q) ((int*)dst)[q] = wds[q];
     }
+  }
+  if (!a.transpose) return;
+  __syncthreads();
+  // column c of the block: keys r0 .. r0+63 at o + c * ld + r0
+  uint8_t* o = (uint8_t*)a.out + ((int64_t)b * a.H + h) * a.d * a.o_ld + r0;
+  for (int e = tid; e < a.d * 16; e += 256) {
+    const int c = e >> 4, j = (e & 15) * 4;
+    int wd = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (j + i < rows) wd |= (int)tile[(j + i) * a.d + c] << (8 * i);
+    *(int*)(o + (int64_t)c * a.o_ld + j) = wd;
   }
 }
 
@@ -141,7 +168,9 @@ struct Fp8Fwd {
 
   struct State {
     int lane, wave, hl, l32;
+    int b, h;
     int q_w0, kv_limit, n_act;
+    float svm;                  // the head's largest V block scale
     const uint8_t* kp;          // K of this (batch, kv-head), key 0
     const uint8_t* vp;          // V^T of this (batch, kv-head), column 0
     const float* ksc;           // K / V block scales of this (batch, kv-head)
@@ -153,7 +182,9 @@ struct Fp8Fwd {
     float lsv_max;              // log2 of the head's largest V block scale
     i32x8 qf[KS];
     f32x16 acc[DT];
-    float m_run, l_run;
+    float m_run;
+    float l_run;                // fp32 sum of p (this lane half's keys): the LSE
+    float l_rnd;                // sum of the E4M3-rounded p (whole row): O's divisor
   };
 
   static __device__ __forceinline__ void issue(const Fp8Args& a, const State& st, int j,
@@ -173,13 +204,18 @@ struct Fp8Fwd {
     }
   }
 
+  static __device__ __forceinline__ i32x8 ones() {
+    const int c = 0x38383838;   // E4M3 1.0 in every byte
+    return i32x8{c, c, c, c, c, c, c, c};
+  }
   static __device__ __forceinline__ i32x8 read32(const char* p) {
     const i32x4 lo = lds_read16<i32x4>(p), hi = lds_read16<i32x4>(p + 16);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 
+  // sk, sv: the tile's K and V block scales
   static __device__ __forceinline__ void tile(const Fp8Args& a, State& st, const char* kb,
-                                              const char* vb, int j) {
+                                              const char* vb, int j, float sk, float sv) {
     const int j0 = j * BC;
     // S^T of the tile's two 32-key blocks
     f32x16 s[2];
@@ -194,15 +230,17 @@ struct Fp8Fwd {
     const int qrow = st.q_w0 + st.l32;
     const bool edge = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
     if (edge) {
+      // relative limits through an empty asm: the compares stay in the branch
+      int lim = st.kv_limit - j0 - 32 * st.hl;
+      int dia = qrow - j0 - 32 * st.hl;
+      asm volatile("" : "+v"(lim), "+v"(dia));
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * st.hl + 16 * blk + r;
-          if (key >= st.kv_limit || (CAUSAL && key > qrow)) s[blk][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (16 * blk + r >= lim || (CAUSAL && 16 * blk + r > dia)) s[blk][r] = -INFINITY;
     }
-    const float cs = st.cq * st.ksc[j];
+    const float cs = st.cq * sk;
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -214,6 +252,7 @@ struct Fp8Fwd {
       if (m_new > st.m_run) {
         const float alpha = (st.m_run == -INFINITY) ? 0.f : fast_exp2(st.m_run - m_new);
         st.l_run *= alpha;
+        st.l_rnd *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
         st.m_run = m_new;
@@ -221,10 +260,10 @@ struct Fp8Fwd {
     }
     const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
     // p' = p sv / svmax 2^7 = exp2(s cs - mref + log2(sv) - log2(svmax) + 7)
-    const float lr = fast_log2(st.vsc[j]) - st.lsv_max + 7.0f;
+    const float lr = fast_log2(sv) - st.lsv_max + 7.0f;
     const float off = lr - mref;
-    float psum = 0.f;
     i32x8 pf;
+    float psum = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int blk = w >> 2, r = (w & 3) * 4;
@@ -236,26 +275,35 @@ struct Fp8Fwd {
       }
       pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
     }
-    // l in units of p: divide the tile's sum by 2^lr
-    st.l_run = __builtin_fmaf(psum, fast_exp2(-lr), st.l_run);
+    // both sums in units of p (over 2^lr); the rounded one from an MFMA
+    // with all-ones codes as A, which puts the column sums of P^T in every row
+    const f32x16 ls = mfma_fp8(ones(), pf, f32x16{});
+    const float rl = fast_exp2(-lr);
+    st.l_run = __builtin_fmaf(psum, rl, st.l_run);
+    st.l_rnd = __builtin_fmaf(ls[0], rl, st.l_rnd);
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       st.acc[dt] = mfma_fp8(read32(vb + st.vbase + dt * 32 * VP), pf, st.acc[dt]);
   }
 
+  // sc: the block scales (K, V) of tile j, loaded one iteration ahead;
+  // replaced by those of tile j+1 (their loads are issued before the barrier
+  // and land while tile j is computed)
   static __device__ __forceinline__ void step(const Fp8Args& a, State& st, int j, int n,
                                               const char* kc, const char* vc, char* kn,
-                                              char* vn) {
+                                              char* vn, float2& sc) {
+    const int jn = min(j + 1, n - 1);
+    const float2 nx = {st.ksc[jn], st.vsc[jn]};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < n) issue(a, st, j + 1, kn, vn);
-    if (j < st.n_act) tile(a, st, kc, vc, j);
+    if (j < st.n_act) tile(a, st, kc, vc, j, sc.x, sc.y);
+    sc = nx;
   }
 
-  static __device__ __forceinline__ void run(const Fp8Args& a, char* k0, char* v0, char* k1,
-                                             char* v1) {
-    State st;
+  // Everything before the key loop; n_tiles: key tiles of this work-group.
+  static __device__ __forceinline__ void setup(const Fp8Args& a, State& st, int& n_tiles) {
     st.lane = threadIdx.x & 63;
     st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     st.hl = st.lane >> 5;
@@ -267,6 +315,8 @@ struct Fp8Fwd {
     const int h = bh % a.Hq, b = bh / a.Hq;
     if (CAUSAL) qblk = a.nqb - 1 - qblk;   // longest rows first
     const int g = h / a.group;
+    st.b = b;
+    st.h = h;
     const int q_blk0 = qblk * ROWS;
     st.q_w0 = q_blk0 + st.wave * 32;
 
@@ -274,7 +324,7 @@ struct Fp8Fwd {
     if (a.kv_lens) st.kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
     int kv_end = st.kv_limit;
     if (CAUSAL) kv_end = min(kv_end, min(q_blk0 + ROWS, a.Nq));
-    const int n_tiles = (kv_end + BC - 1) / BC;
+    n_tiles = (kv_end + BC - 1) / BC;
     st.n_act = CAUSAL ? min(n_tiles, (st.q_w0 + 31) / BC + 1) : n_tiles;
 
     st.kp = a.k + b * a.k_sb + g * a.k_sh;
@@ -323,22 +373,39 @@ struct Fp8Fwd {
     for (int t = st.lane; t < n_tiles; t += 64) svm = fmaxf(svm, st.vsc[t]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) svm = fmaxf(svm, __shfl_xor(svm, o, 64));
+    st.svm = svm;
     st.lsv_max = svm > 0.f ? fast_log2(svm) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
     st.m_run = -INFINITY;
     st.l_run = 0.f;
+    st.l_rnd = 0.f;
+  }
 
-    if (n_tiles > 0) issue(a, st, 0, k0, v0);
-    for (int j = 0; j < n_tiles; j += 2) {
-      step(a, st, j, n_tiles, k0, v0, k1, v1);
-      if (j + 1 >= n_tiles) break;
-      step(a, st, j + 1, n_tiles, k1, v1, k0, v0);
+  static __device__ __forceinline__ void run(const Fp8Args& a, char* k0, char* v0, char* k1,
+                                             char* v1) {
+    State st;
+    int n_tiles;
+    setup(a, st, n_tiles);
+    float2 sc = {1.f, 1.f};
+    if (n_tiles > 0) {
+      issue(a, st, 0, k0, v0);
+      sc = float2{st.ksc[0], st.vsc[0]};
     }
+    for (int j = 0; j < n_tiles; j += 2) {
+      step(a, st, j, n_tiles, k0, v0, k1, v1, sc);
+      if (j + 1 >= n_tiles) break;
+      step(a, st, j + 1, n_tiles, k1, v1, k0, v0, sc);
+    }
+    epilogue(a, st);
+  }
 
-    T* op = (T*)a.o + b * a.o_sb + h * a.o_sh;
+  // O = acc svmax 2^-7 / l_rnd (the row-sum MFMA already covers both lane
+  // halves), LSE = ln2 (m + log2 l) with the fp32 sum l of both halves.
+  static __device__ __forceinline__ void epilogue(const Fp8Args& a, const State& st) {
+    T* op = (T*)a.o + st.b * a.o_sb + st.h * a.o_sh;
     const float l_tot = add_with_other_half(st.l_run);
-    const float inv = l_tot > 0.f ? svm * 0.0078125f / l_tot : 0.f;   // svmax 2^-7 / l
+    const float inv = st.l_rnd > 0.f ? st.svm * 0.0078125f / st.l_rnd : 0.f;
     const int row = st.q_w0 + st.l32;
     if (row < a.Nq) {
 #pragma unroll
@@ -353,7 +420,7 @@ struct Fp8Fwd {
           }
         }
       if (st.hl == 0)
-        a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] =
+        a.lse[((int64_t)st.b * a.Hq + st.h) * a.Nq + row] =
             l_tot > 0.f ? (st.m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
   }
