@@ -25,19 +25,21 @@
 //                  of 32-key block blk makes register r of lane half h hold
 //                  key 32 h + 16 blk + r, so a lane half holds 32
 //                  consecutive keys.
-//   softmax        p = exp2(s c sq sk - m + log2(sv / svmax) + 7), with the
-//                  reference m moved lazily by more than 1 (so p <= 256 <
-//                  448); the V block scale sv enters through p (relative to
-//                  the head's largest svmax) and the factor 2^7 keeps small
-//                  p out of E4M3's subnormal range;
+//   softmax        p = exp2(s c sq sk - m + log2(sv / svmax) + 6), with the
+//                  reference m moved lazily, only when a tile exceeds it by
+//                  more than 2.75 (so p <= 2^8.75 < 448); the V block scale
+//                  sv enters through p (relative to the head's largest
+//                  svmax) and the factor 2^6 keeps p above E4M3's subnormal
+//                  range down to 2^-12 of the row's largest weight;
 //   O^T += V^T P^T  P packed to E4M3 (slot 16 blk + r = key 32 h + 16 blk + r)
 //                  as the B operand; A = 32 consecutive keys of a V^T row;
 //   sums           one more MFMA with all-ones codes as A sums the rounded
 //                  P over the tile's keys (every row of its result holds
 //                  the column sums), the divisor of O; an fp32 sum of the
 //                  unrounded p gives the LSE.
+// All 16 LDS fragment reads of a tile are issued before its first MFMA.
 // The block scales of tile j+1 are loaded before the barrier of tile j.
-// Epilogue: O = acc * svmax * 2^-7 / l_rounded, LSE = ln2 (m + log2 l).
+// Epilogue: O = acc * svmax * 2^-6 / l_rounded, LSE = ln2 (m + log2 l).
 #include "attn_kernels.h"
 #include "device_common.h"
 
@@ -162,7 +164,9 @@ struct Fp8Fwd {
   static constexpr int K_BYTES = BC * KP, V_BYTES = D * VP;
   static constexpr int K_INS = (BC * KPS + 63) / 64, V_INS = (D * VPS + 63) / 64;
   static constexpr int K_IPW = (K_INS + NW - 1) / NW, V_IPW = (V_INS + NW - 1) / NW;
-  static constexpr float TH = 1.0f;                    // lazy rescale threshold (log2)
+  static constexpr float TH = 2.75f;                   // lazy rescale threshold (log2)
+  static constexpr float PSHIFT = 6.0f;                // log2 of p's scale factor
+  static_assert(TH + PSHIFT < 8.807f, "p must stay below E4M3's 448");
   using T = typename E::T;
   using V4 = typename E::V4;
 
@@ -185,6 +189,7 @@ struct Fp8Fwd {
     float m_run;
     float l_run;                // fp32 sum of p (this lane half's keys): the LSE
     float l_rnd;                // sum of the E4M3-rounded p (whole row): O's divisor
+    i32x8 one;                  // E4M3 1.0 in every byte (A of the row-sum MFMA)
   };
 
   static __device__ __forceinline__ void issue(const Fp8Args& a, const State& st, int j,
@@ -217,14 +222,23 @@ struct Fp8Fwd {
   static __device__ __forceinline__ void tile(const Fp8Args& a, State& st, const char* kb,
                                               const char* vb, int j, float sk, float sv) {
     const int j0 = j * BC;
+    // every LDS fragment of the tile first (K for S^T, V^T for PV), so the
+    // reads overlap each other and the first products
+    i32x8 kf[2 * KS], vf[DT];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[blk * KS + ks] = read32(kb + st.kbase + blk * 16 * KP + ks * 64);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = read32(vb + st.vbase + dt * 32 * VP);
+    __builtin_amdgcn_sched_barrier(0);
     // S^T of the tile's two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[blk] = mfma_fp8(read32(kb + st.kbase + blk * 16 * KP + ks * 64), st.qf[ks], s[blk]);
+      for (int ks = 0; ks < KS; ++ks) s[blk] = mfma_fp8(kf[blk * KS + ks], st.qf[ks], s[blk]);
     }
     // register r of block blk: key j0 + 32 hl + 16 blk + r
     const int qrow = st.q_w0 + st.l32;
@@ -259,11 +273,11 @@ struct Fp8Fwd {
       }
     }
     const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
-    // p' = p sv / svmax 2^7 = exp2(s cs - mref + log2(sv) - log2(svmax) + 7)
-    const float lr = fast_log2(sv) - st.lsv_max + 7.0f;
+    // p' = p sv / svmax 2^6 = exp2(s cs - mref + log2(sv) - log2(svmax) + 6)
+    const float lr = fast_log2(sv) - st.lsv_max + PSHIFT;
     const float off = lr - mref;
     i32x8 pf;
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int blk = w >> 2, r = (w & 3) * 4;
@@ -271,20 +285,23 @@ struct Fp8Fwd {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[i] = fast_exp2(__builtin_fmaf(s[blk][r + i], cs, off));
-        psum += p[i];
+        psum = (w == 0 && i == 0) ? p[0] : psum + p[i];
       }
-      pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+      // the high half of the first conversion's old value is overwritten by
+      // the second: any register will do (no zeroing move)
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_bit_cast(int, p[0]), false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
     }
     // both sums in units of p (over 2^lr); the rounded one from an MFMA
     // with all-ones codes as A, which puts the column sums of P^T in every row
-    const f32x16 ls = mfma_fp8(ones(), pf, f32x16{});
+    const f32x16 ls = mfma_fp8(st.one, pf, f32x16{});
     const float rl = fast_exp2(-lr);
     st.l_run = __builtin_fmaf(psum, rl, st.l_run);
     st.l_rnd = __builtin_fmaf(ls[0], rl, st.l_rnd);
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      st.acc[dt] = mfma_fp8(read32(vb + st.vbase + dt * 32 * VP), pf, st.acc[dt]);
+      st.acc[dt] = mfma_fp8(vf[dt], pf, st.acc[dt]);
   }
 
   // sc: the block scales (K, V) of tile j, loaded one iteration ahead;
@@ -378,6 +395,9 @@ struct Fp8Fwd {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
     st.m_run = -INFINITY;
+    // kept in registers for the whole loop (not rematerialised every tile)
+    st.one = ones();
+    asm volatile("" : "+v"(st.one));
     st.l_run = 0.f;
     st.l_rnd = 0.f;
   }
@@ -400,12 +420,12 @@ struct Fp8Fwd {
     epilogue(a, st);
   }
 
-  // O = acc svmax 2^-7 / l_rnd (the row-sum MFMA already covers both lane
+  // O = acc svmax 2^-6 / l_rnd (the row-sum MFMA already covers both lane
   // halves), LSE = ln2 (m + log2 l) with the fp32 sum l of both halves.
   static __device__ __forceinline__ void epilogue(const Fp8Args& a, const State& st) {
     T* op = (T*)a.o + st.b * a.o_sb + st.h * a.o_sh;
     const float l_tot = add_with_other_half(st.l_run);
-    const float inv = st.l_rnd > 0.f ? st.svm * 0.0078125f / st.l_rnd : 0.f;
+    const float inv = st.l_rnd > 0.f ? st.svm * 0.015625f / st.l_rnd : 0.f;
     const int row = st.q_w0 + st.l32;
     if (row < a.Nq) {
 #pragma unroll
@@ -427,7 +447,7 @@ struct Fp8Fwd {
 };
 
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(Fp8Args a) {
   using K = Fp8Fwd<E, D, CAUSAL>;
   __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];

@@ -7,12 +7,15 @@
   attention on the dequantised inputs (ref_fwd_fp8).  Its one approximation
   is the rounding of the probabilities to E4M3 for the product with V; each
   rounding errs by at most 2^-4 of the probability, or 2^-10 in the kernel's
-  scaled units (2^-17 / ratio of a probability, ratio = the tile's V scale
-  over the head's largest) where it falls below E4M3's normal range.  O is
+  scaled units where it falls below E4M3's normal range.  The kernel scales p
+  by 2^6 sv / svmax relative to a reference no larger than the row's
+  maximum, so the row's largest weight is at least 2^6 ratio (ratio = the
+  tile's V scale over the head's largest) and a subnormal rounding is at
+  most 2^-16 / ratio of the row's total weight.  O is
   divided by the sum of the rounded weights, so
   O - O_ref = sum_j (p~_j - p_j)(v_j - O_ref) / sum_j p~_j, and per element
       |O - O_ref|_ic <= c sum_j P_ij |v_jc - O_ref_ic|
-                        + 2^-17 / ratio_min sum_j |v_jc - O_ref_ic| / (1 - 2^-4)
+                        + 2^-16 / ratio_min sum_j |v_jc - O_ref_ic| / (1 - 2^-4)
                         + 2^-8 |O_ref_ic| + 1e-6,   c = 2^-4 / (1 - 2^-4)
   (the third term covers the 16-bit output rounding and fp32 sums), with P
   and v the oracle's probabilities and dequantised values.  LSE comes from
@@ -107,7 +110,7 @@ def _check_fp8(o, lse, O_ref, L_ref, P, Vd, vsc, G, label, out_dtype):
             for i in range(O_ref.shape[2]):
                 dev = np.abs(v - O_ref[bb, hh, i])       # |v_j - O_i| per key and column
                 bound[bb, hh, i] = (c * (P[bb, hh, i] @ dev)
-                                    + 2.0 ** -17 / (1 - 2.0 ** -4) / ratio_min[bb, hh // G]
+                                    + 2.0 ** -16 / (1 - 2.0 ** -4) / ratio_min[bb, hh // G]
                                     * dev.sum(axis=0))
     bound += 2.0 ** -8 * np.abs(O_ref) + 1e-6
     worst = float((err / bound).max()) if err.size else 0.0
