@@ -9,9 +9,11 @@
 // Work decomposition: one work-group of NW waves per (batch, q-head, block of
 // NW*32 query rows); each wave owns 32 rows, whose Q fragments stay in
 // registers.  K/V tiles of BC keys stream through LDS (padded row pitches),
-// double-buffered and filled by direct global->LDS loads: the load of tile
-// j+1 runs while tile j is in use.  With NW = 8 (two waves per SIMD) the waves of a SIMD overlap
-// each other's LDS and VALU latency.
+// filled by direct global->LDS loads: at d = 128 double-buffered (the load of
+// tile j+1 runs while tile j is in use), at d <= 64 in three stages (loads two
+// tiles ahead; such a tile is too short to cover one load).  With NW = 8 (two
+// waves per SIMD) the waves of a SIMD overlap each other's LDS and VALU
+// latency.
 //
 // Per KV tile and wave:
 //   S^T = K_j Q^T        32x32x16 MFMA, A = K from LDS, B = Q from registers;
@@ -71,6 +73,12 @@ struct FwdKernel {
   static constexpr int V_INS = (BC * VPS + 63) / 64;
   static constexpr int K_IPW = (K_INS + NW - 1) / NW;  // ... per wave
   static constexpr int V_IPW = (V_INS + NW - 1) / NW;
+  // LDS stages.  At d <= 64 a tile is too short to cover a load issued one
+  // tile ahead, so three stages (loads two tiles ahead) are kept; three still
+  // leave room for two work-groups per CU.  At d = 128 two.
+  static constexpr int NST = D <= 64 ? 3 : 2;
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "stages start on 1 KB boundaries");
   static constexpr int ROWS = NW * 32;              // query rows per block
   static constexpr int KB = BC / 32;                // 32-key blocks per tile
   static constexpr int KS = D / 16;                 // k-steps of QK^T
@@ -87,6 +95,7 @@ struct FwdKernel {
     int q_w0;                   // first query row of this wave
     int kv_limit;               // keys >= kv_limit are excluded
     int n_act;                  // tiles this wave has to visit (causal)
+    int dma_n;                  // DMA instructions this wave issues per tile
     int t_lo, t_hi;             // LOCAL: this wave's tiles [t_lo, t_hi)
     LocalVis::Row lrow;         // LOCAL: this lane's query position
     const char* kp;             // K / V of this (batch, kv-head), key 0
@@ -241,11 +250,34 @@ struct FwdKernel {
     }
   }
 
+  // Tile j with loads kept two tiles ahead (NST = 3): this wave's share of
+  // tile j has landed once at most the dma_n loads of tile j+1 are
+  // outstanding; after the barrier every wave's share has, and every wave is
+  // done with tile j-1, whose stage takes tile j+2.  A plain s_barrier: the
+  // workgroup fence of __syncthreads would wait for tile j+1 as well.  The
+  // empty asm statements keep LDS accesses on their side of it.
+  static __device__ __forceinline__ void step3(const FwdArgs& a, State& st, int j, int t_end,
+                                               const char* kc, const char* vc, char* kn, char* vn) {
+    if (j + 1 < t_end) wait_vmem(st.dma_n);
+    else wait_vmem(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 2 < t_end) issue(st, (j + 2) * BC, kn, vn);
+    body(a, st, j, kc, vc);
+  }
+
   static __device__ __forceinline__ void step(const FwdArgs& a, State& st, int j, int t_end,
                                               const char* kc, const char* vc, char* kn, char* vn) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile j has landed
     __syncthreads();
     if (j + 1 < t_end) issue(st, (j + 1) * BC, kn, vn);
+    body(a, st, j, kc, vc);
+  }
+
+  // tile j unless this wave has nothing to do in it
+  static __device__ __forceinline__ void body(const FwdArgs& a, State& st, int j, const char* kc,
+                                              const char* vc) {
     if constexpr (LOCAL) {
       if (j >= st.t_lo && j < st.t_hi) {
         const uint64_t bits = a.loc.bits(st.lrow, j * BC, st.kv_limit);
@@ -256,8 +288,9 @@ struct FwdKernel {
     }
   }
 
-  static __device__ __forceinline__ void run(const FwdArgs& a, char* k0, char* v0, char* k1,
-                                             char* v1) {
+  static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
+    auto kb = [&](int s) { return lds + s * STAGE_BYTES; };
+    auto vb = [&](int s) { return lds + s * STAGE_BYTES + K_BYTES; };
     State st;
     st.lane = threadIdx.x & 63;
     st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -281,8 +314,10 @@ struct FwdKernel {
     int kv_end = st.kv_limit;
     if (CAUSAL) kv_end = min(kv_end, min(q_blk0 + ROWS, a.Nq));
     const int n_tiles = (kv_end + BC - 1) / BC;
-    // causal: a wave sees no key beyond its last row
+    // causal: a wave sees no key beyond its last row; a wave whose rows all
+    // lie past Nq only helps with the loads
     st.n_act = CAUSAL ? min(n_tiles, (st.q_w0 + 31) / BC + 1) : n_tiles;
+    if (st.q_w0 >= a.Nq) st.n_act = 0;
     const int dchunks = a.d / 8;
     st.c = a.c;
     st.kp = (const char*)((const T*)a.k + b * a.k_sb + g * a.k_sh);
@@ -297,6 +332,11 @@ struct FwdKernel {
 #pragma unroll
     for (int i = 0; i < V_IPW; ++i)
       st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn);
+    st.dma_n = 0;
+#pragma unroll
+    for (int i = 0; i < K_IPW; ++i) st.dma_n += i * NW + st.wave < K_INS;
+#pragma unroll
+    for (int i = 0; i < V_IPW; ++i) st.dma_n += i * NW + st.wave < V_INS;
     // K read: lane holds key row l32 (+32 k), chunk 2 ks + hl.
     st.kbase = st.l32 * KP + st.hl * 16;
     // V transposed read: in each 16-lane group lane i points at row
@@ -336,11 +376,22 @@ struct FwdKernel {
       }
       st.lrow = a.loc.row(min(st.q_w0 + st.l32, a.Nq - 1));
     }
-    if (t_begin < t_end) issue(st, t_begin * BC, k0, v0);
-    for (int j = t_begin; j < t_end; j += 2) {
-      step(a, st, j, t_end, k0, v0, k1, v1);
-      if (j + 1 >= t_end) break;
-      step(a, st, j + 1, t_end, k1, v1, k0, v0);
+    if (t_begin < t_end) issue(st, t_begin * BC, kb(0), vb(0));
+    if constexpr (NST == 2) {
+      for (int j = t_begin; j < t_end; j += 2) {
+        step(a, st, j, t_end, kb(0), vb(0), kb(1), vb(1));
+        if (j + 1 >= t_end) break;
+        step(a, st, j + 1, t_end, kb(1), vb(1), kb(0), vb(0));
+      }
+    } else {
+      if (t_begin + 1 < t_end) issue(st, (t_begin + 1) * BC, kb(1), vb(1));
+      for (int j = t_begin; j < t_end; j += 3) {
+        step3(a, st, j, t_end, kb(0), vb(0), kb(2), vb(2));
+        if (j + 1 >= t_end) break;
+        step3(a, st, j + 1, t_end, kb(1), vb(1), kb(0), vb(0));
+        if (j + 2 >= t_end) break;
+        step3(a, st, j + 2, t_end, kb(2), vb(2), kb(1), vb(1));
+      }
     }
 
     // Epilogue.
@@ -374,11 +425,8 @@ template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK, bool LOCAL = f
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void fwd_kernel(FwdArgs a) {
   using K = FwdKernel<E, D, NW, BC, CAUSAL, MASK, LOCAL, SOFTCAP>;
-  __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v1[K::V_BYTES];
-  K::run(a, k0, v0, k1, v1);
+  __shared__ __attribute__((aligned(1024))) char lds[K::NST * K::STAGE_BYTES];
+  K::run(a, lds);
 }
 
 }  // namespace attn

@@ -97,6 +97,24 @@ __device__ __forceinline__ void dma16(const void* gsrc, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (LDS_AS void*)lds_wave_base, 16, 0, 0);
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..7 (larger n waits for all):
+// at most n vector-memory operations of this wave, the latest issued, stay
+// outstanding.  expcnt and lgkmcnt are left at their maxima (no wait); the
+// gfx9 encoding keeps vmcnt's low bits in [3:0], expcnt in [6:4], lgkmcnt in
+// [11:8].
+__device__ __forceinline__ void wait_vmem(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_s_waitcnt(0xF71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+    default: __builtin_amdgcn_s_waitcnt(0xF70); break;
+  }
+}
+
 // Raw buffer resource over [base, base + bytes): loads at offsets at or past
 // `bytes` return zero instead of touching memory.  The last descriptor word
 // selects a raw buffer with 32-bit data format (gfx9 family encoding).
