@@ -315,7 +315,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the attention of every (batch, head) is "
-              f"independent and this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              f"independent and the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
