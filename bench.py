@@ -42,9 +42,11 @@ DEFAULT_WORKLOAD = "long_bf16_b8_h32_n4096_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_long_bf16_b8_h32_n4096_d128_traffic.txt")
 # Workloads whose floor is HBM bandwidth (or launch latency) rather than MFMA
 HBM_BOUND = ("vit_bf16_b128_h16_n196_d64", "unet_cross_fp16_b2_h8_q4096_k77_d40")
+# The sources the measured forward kernel (fwd_pipe_kernel) and its launch are
+# built from: its counters stay valid while these are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_25_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "attn_fwd_kernel.h", "attn_fwd_pipe_kernel.h",
-                            "device_common.h", "attn_kernels.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_pipe_kernel.h", "device_common.h",
+                            "attn_kernels.h", "local_mask.h")]
 
 
 def is_local(w) -> bool:

@@ -190,13 +190,18 @@ struct FwdKernel {
     } else {
       const bool edge = (j0 + BC > st.kv_limit) || (CAUSAL && j0 + BC - 1 > st.q_w0);
       if (edge) {
+        // register r of block k holds key j0 + 4 hl + k*32 + (r/4)*8 + r%4: one
+        // limit per lane relative to j0 + 4 hl (key lengths and the diagonal
+        // together), so each element costs a compare with a constant and a
+        // select; the empty asm keeps the compares in this branch
+        int lim = st.kv_limit - j0 - 4 * st.hl;
+        if (CAUSAL) lim = min(lim, qrow + 1 - j0 - 4 * st.hl);
+        asm volatile("" : "+v"(lim));
 #pragma unroll
         for (int k = 0; k < KB; ++k)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + k * 32 + (r >> 2) * 8 + st.hl * 4 + (r & 3);
-            if (key >= st.kv_limit || (CAUSAL && key > qrow)) s[k][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (k * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[k][r] = -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -207,12 +212,17 @@ struct FwdKernel {
     mx = max_with_other_half(mx);
     const float cand = PRE ? mx : mx * st.c;
     if (__builtin_amdgcn_ballot_w64(cand > st.m_run + kRescaleThreshold)) {
+      // while no row of the wave has a finite reference point O and l are
+      // still zero: nothing to rescale
+      const bool any_ref = __builtin_amdgcn_ballot_w64(st.m_run != -INFINITY) != 0;
       const float m_new = fmaxf(st.m_run, cand);
       if (m_new > st.m_run) {
-        const float alpha = (st.m_run == -INFINITY) ? 0.f : fast_exp2(st.m_run - m_new);
-        st.l_run *= alpha;
+        if (any_ref) {
+          const float alpha = (st.m_run == -INFINITY) ? 0.f : fast_exp2(st.m_run - m_new);
+          st.l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+          for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+        }
         st.m_run = m_new;
       }
     }
