@@ -14,7 +14,9 @@
 //
 //   phase 1 (NQ steps):  one QK^T MFMA of tile j+1 per step, interleaved with
 //                        part of tile j's exponentials (p = exp2(s*c - m),
-//                        row sum, conversion to the 16-bit P operand);
+//                        row sum, conversion to the 16-bit P operand), and
+//                        at every other step one of this wave's loads of
+//                        V(j+1) / K(j+2) into the buffers iteration j-1 used;
 //   phase 2 (NP steps):  one PV MFMA of tile j per step; the first half of
 //                        the steps finish the exponentials (each 16-key
 //                        chunk before its first PV), the second half reduce
@@ -172,7 +174,25 @@ struct FwdPipeKernel {
   // tile vc) with S of tile j+1 (into sn, from K tile kn).  Returns this
   // lane's share of tile j+1's unmasked row maximum.
   static __device__ __forceinline__ float main_block(State& st, const Scores& sc, Scores& sn,
-                                                     const char* kn, const char* vc) {
+                                                     const char* kn, const char* vc, int j, int n,
+                                                     char* kdst, char* vdst) {
+    // This iteration's loads (V(j+1), then K(j+2)), one at every other
+    // phase-1 step: issued together after the barrier, the 8 waves' loads
+    // queue behind each other and hold the last waves back by ~600 cycles.
+    const bool do_v = j + 1 < n, do_k = j + 2 < n;
+    const int64_t vo = (int64_t)(j + 1) * st.v_tile, ko = (int64_t)(j + 2) * st.k_tile;
+    const BufRsrc rv = make_rsrc(st.vp + vo, (uint32_t)min(st.v_end - vo, (int64_t)kBufLimit));
+    const BufRsrc rk = make_rsrc(st.kp + ko, (uint32_t)min(st.k_end - ko, (int64_t)kBufLimit));
+    auto load_one = [&](int x) {
+      if (x < V_IPW) {
+        const int ins = x * NW + st.wave;
+        if (do_v && ins < V_INS) dma16_buf(rv, st.voff[x], vdst + ins * 1024);
+      } else if (x < V_IPW + K_IPW) {
+        const int ins = (x - V_IPW) * NW + st.wave;
+        if (do_k && ins < K_INS) dma16_buf(rk, st.koff[x - V_IPW], kdst + ins * 1024);
+      }
+    };
+    static_assert(V_IPW + K_IPW <= (NQ + 1) / 2, "the loads fit in phase 1");
     const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
     float lsum = 0.f;
     V2 pp[NPAIR];
@@ -206,8 +226,13 @@ struct FwdPipeKernel {
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = lds_read16<V8>(kaddr(st, kn, i));
     // phase 1
+    // In phase 1 the older wave of each SIMD pair (waves 0..3) otherwise wins
+    // the issue arbitration and the younger one finishes ~80 % later; raising
+    // the younger wave's priority for phase 1 evens them out a little.
+    if (st.wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
+      if ((i & 1) == 0) load_one(i >> 1);
       if (i + PF < NQ) kf[i + PF] = lds_read16<V8>(kaddr(st, kn, i + PF));
       else vload(i + PF - NQ);
       sn[i % KB] = E::mfma(kf[i], st.qf[i / KB], sn[i % KB]);
@@ -215,6 +240,7 @@ struct FwdPipeKernel {
       for (int p = (i * P1) / NQ; p < ((i + 1) * P1) / NQ; ++p) pair(p);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (st.wave >= NW / 2) __builtin_amdgcn_s_setprio(0);
     // phase 2
     float mx = -INFINITY;
 #pragma unroll
@@ -238,15 +264,12 @@ struct FwdPipeKernel {
     return mx;
   }
 
-  // Top of iteration j: K(j+1) and V(j) (issued one iteration ago) have
-  // landed for every wave once all pass the barrier; then K(j+2) and V(j+1)
-  // go into the buffers iteration j-1 has finished with.
-  static __device__ __forceinline__ void sync_and_issue(const State& st, int j, int n,
-                                                        char* kdst, char* vdst) {
+  // Top of iteration j: K(j+1) and V(j) (loaded during iteration j-1) have
+  // landed for every wave once all pass the barrier; K(j+2) and V(j+1) then
+  // go, during iteration j, into the buffers iteration j-1 has finished with.
+  static __device__ __forceinline__ void sync(const State& st) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < n) issue_v(st, j + 1, vdst);
-    if (j + 2 < n) issue_k(st, j + 2, kdst);
   }
 
   // After the main block of iteration j: tile j+1's maximum and rescale.
@@ -335,11 +358,11 @@ struct FwdPipeKernel {
       // last tile that result is not used (the K buffer then holds stale
       // data, which is harmless).
       for (int j = 0; j < n_tiles; j += 2) {
-        sync_and_issue(st, j, n_tiles, k0, v1);
-        finish_next(st, s1, j, main_block(st, s0, s1, k1, v0));
+        sync(st);
+        finish_next(st, s1, j, main_block(st, s0, s1, k1, v0, j, n_tiles, k0, v1));
         if (j + 1 >= n_tiles) break;
-        sync_and_issue(st, j + 1, n_tiles, k1, v0);
-        finish_next(st, s0, j + 1, main_block(st, s1, s0, k0, v1));
+        sync(st);
+        finish_next(st, s0, j + 1, main_block(st, s1, s0, k0, v1, j + 1, n_tiles, k1, v0));
       }
     }
 
