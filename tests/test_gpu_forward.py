@@ -100,6 +100,38 @@ def test_forward_small(gpu_lib, case):
     check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
 
 
+# At d <= 64 the forward streams key tiles through three LDS stages whose
+# roles rotate with the tile index (loads run two tiles ahead): every key-tile
+# count from 1 to 7, so each count modulo 3 ends the loop at each stage, with
+# causal rows (per-wave tile counts), key lengths, an additive mask, GQA,
+# BNHD and ragged last tiles.  Nk < 512 keeps these on that kernel.
+STAGES = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mask, layout
+    ("tiles1_d64", 2, 2, 1, 40, 50, 64, "bf16", False, None, None, "bhnd"),
+    ("tiles2_d64_fp16", 1, 2, 2, 70, 128, 64, "fp16", False, None, None, "bhnd"),
+    ("tiles3_d40", 2, 2, 2, 100, 150, 40, "bf16", False, None, None, "bhnd"),
+    ("tiles4_causal_d64", 1, 2, 1, 256, 256, 64, "bf16", True, None, None, "bhnd"),
+    ("tiles4_5_lens_d64", 2, 2, 2, 130, 320, 64, "fp16", False, (200, 320), None, "bhnd"),
+    ("tiles5_mask_d64", 1, 2, 2, 90, 300, 64, "bf16", False, None, "full11", "bhnd"),
+    ("tiles6_d32", 2, 2, 1, 64, 383, 32, "bf16", False, None, None, "bhnd"),
+    ("tiles7_causal_gqa_d64", 1, 4, 2, 448, 448, 64, "bf16", True, None, None, "bhnd"),
+    ("tiles7_d48_bnhd", 1, 3, 3, 100, 447, 48, "fp16", False, None, None, "bnhd"),
+]
+
+
+@pytest.mark.parametrize("case", STAGES, ids=[c[0] for c in STAGES])
+def test_forward_stage_rotation(gpu_lib, case):
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mkind, layout = case
+    _say(f"[fwd-stages] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens)
+    mask = _mask(mkind, B, Hq, Nq, Nk, np.random.default_rng(11))
+    o, lse = _run(w, x, layout=layout, causal=causal, mask=mask)
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], causal=causal, mask=mask,
+                           kv_lens=x["kv_lens"])
+    check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
+
+
 def test_forward_empty_and_no_keys(gpu_lib):
     import torch
     from exact_attention_25_amd import binding as bd
