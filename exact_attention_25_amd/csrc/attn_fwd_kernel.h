@@ -96,6 +96,9 @@ struct FwdKernel {
     int kv_limit;               // keys >= kv_limit are excluded
     int n_act;                  // tiles this wave has to visit (causal)
     int dma_n;                  // DMA instructions this wave issues per tile
+    int ld_j0;                  // first key of the tile to load during this tile (-1: none)
+    char* ld_kb;
+    char* ld_vb;
     int t_lo, t_hi;             // LOCAL: this wave's tiles [t_lo, t_hi)
     LocalVis::Row lrow;         // LOCAL: this lane's query position
     const char* kp;             // K / V of this (batch, kv-head), key 0
@@ -146,12 +149,29 @@ struct FwdKernel {
   // iff key j0 + i is visible to this lane's row.
   static __device__ __forceinline__ void tile(const FwdArgs& a, State& st, const char* kbuf,
                                               const char* vbuf, int j0, uint64_t bits) {
-    // S^T = K_j Q^T
+    // S^T = K_j Q^T, with this wave's loads of the next tile (ld_j0, if any)
+    // spread over its first MFMAs: issued together after the barrier, the 8
+    // waves' loads queue behind each other and hold the last waves back
+    const bool ld = st.ld_j0 >= 0;
+    const int64_t lko = (int64_t)(st.ld_j0 / BC) * st.k_tile, lvo = (int64_t)(st.ld_j0 / BC) * st.v_tile;
+    const BufRsrc lrk = make_rsrc(st.kp + lko, (uint32_t)min(st.k_end - lko, (int64_t)kBufLimit));
+    const BufRsrc lrv = make_rsrc(st.vp + lvo, (uint32_t)min(st.v_end - lvo, (int64_t)kBufLimit));
+    auto load_one = [&](int x) {
+      if (!ld) return;
+      if (x < K_IPW) {
+        const int ins = x * NW + st.wave;
+        if (ins < K_INS) dma16_buf(lrk, st.koff[x], st.ld_kb + ins * 1024);
+      } else if (x < K_IPW + V_IPW) {
+        const int ins = (x - K_IPW) * NW + st.wave;
+        if (ins < V_INS) dma16_buf(lrv, st.voff[x - K_IPW], st.ld_vb + ins * 1024);
+      }
+    };
     f32x16 s[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) s[k] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      if (ks * 2 < K_IPW + V_IPW) { load_one(ks * 2); load_one(ks * 2 + 1); }
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
         const V8 kf = lds_read16<V8>(kbuf + st.kbase + k * 32 * KP + ks * 32);
@@ -273,7 +293,9 @@ struct FwdKernel {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (j + 2 < t_end) issue(st, (j + 2) * BC, kn, vn);
+    st.ld_j0 = j + 2 < t_end ? (j + 2) * BC : -1;
+    st.ld_kb = kn;
+    st.ld_vb = vn;
     body(a, st, j, kc, vc);
   }
 
@@ -281,22 +303,33 @@ struct FwdKernel {
                                               const char* kc, const char* vc, char* kn, char* vn) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile j has landed
     __syncthreads();
-    if (j + 1 < t_end) issue(st, (j + 1) * BC, kn, vn);
+    st.ld_j0 = j + 1 < t_end ? (j + 1) * BC : -1;
+    st.ld_kb = kn;
+    st.ld_vb = vn;
     body(a, st, j, kc, vc);
   }
 
   // tile j unless this wave has nothing to do in it
   static __device__ __forceinline__ void body(const FwdArgs& a, State& st, int j, const char* kc,
                                               const char* vc) {
+    bool done = false;
     if constexpr (LOCAL) {
       if (j >= st.t_lo && j < st.t_hi) {
         const uint64_t bits = a.loc.bits(st.lrow, j * BC, st.kv_limit);
-        if (__builtin_amdgcn_ballot_w64(bits != 0)) tile(a, st, kc, vc, j * BC, bits);
+        if (__builtin_amdgcn_ballot_w64(bits != 0)) {
+          tile(a, st, kc, vc, j * BC, bits);
+          done = true;
+        }
       }
     } else {
-      if (j < st.n_act) tile(a, st, kc, vc, j * BC, 0);
+      if (j < st.n_act) {
+        tile(a, st, kc, vc, j * BC, 0);
+        done = true;
+      }
     }
+    if (!done && st.ld_j0 >= 0) issue(st, st.ld_j0, st.ld_kb, st.ld_vb);
   }
+
 
   static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
     auto kb = [&](int s) { return lds + s * STAGE_BYTES; };
