@@ -75,8 +75,8 @@ def fwd_kernel_name(w) -> str:
     if is_local(w) or w.softcap:
         return (f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal and not is_local(w)).lower()},"
                 f"mask=false,local={str(is_local(w)).lower()},softcap={str(bool(w.softcap)).lower()}>")
-    if not w.causal and w.Nk >= 8 * 64:
-        return f"attn::fwd_pipe_kernel<{e},{D},64>"
+    if (min(w.Nq, w.Nk) if w.causal else w.Nk) >= 8 * 64:
+        return f"attn::fwd_pipe_kernel<{e},{D},64,causal={str(w.causal).lower()}>"
     return f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal).lower()},mask=false>"
 
 

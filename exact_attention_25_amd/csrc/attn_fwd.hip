@@ -1,6 +1,7 @@
-// Forward attention: kernel instances and dispatch.  Calls without a causal
-// or additive mask and with at least 8 key tiles take the software-pipelined
-// kernel (attn_fwd_pipe_kernel.h); the others take FwdKernel
+// Forward attention: kernel instances and dispatch.  Calls without an
+// additive mask whose work-groups see at least 8 key tiles (causal: min(Nq,
+// Nk) >= 8 tiles) take the software-pipelined kernel
+// (attn_fwd_pipe_kernel.h); the others take FwdKernel
 // (attn_fwd_kernel.h).  Both compute the same values.  Local and
 // soft-capped calls go to attn_fwd_local.hip.
 #include "attn_fwd_kernel.h"
@@ -12,12 +13,17 @@ template <class E, int D, int NW, int BC>
 static hipError_t launch_fwd_t(const FwdArgs& a0, bool causal, bool mask, hipStream_t st) {
   // The pipelined kernel computes one tile more than it uses and has a longer
   // prologue, which short key ranges do not amortise.
-  if (!causal && !mask && a0.Nk >= 8 * BC) {
-    using P = FwdPipeKernel<E, D, BC>;
+  if (!mask && (causal ? min(a0.Nq, a0.Nk) : a0.Nk) >= 8 * BC) {
+    using P = FwdPipeKernel<E, D, BC, false>;
     FwdArgs a = a0;
     a.nqb = (a.Nq + P::ROWS - 1) / P::ROWS;
     a.total_blocks = a.B * a.Hq * a.nqb;
-    hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC>), dim3(a.total_blocks), dim3(P::NW * 64), 0, st, a);
+    if (causal)
+      hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC, true>), dim3(a.total_blocks), dim3(P::NW * 64),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC, false>), dim3(a.total_blocks), dim3(P::NW * 64),
+                         0, st, a);
     return hipGetLastError();
   }
   using K = FwdKernel<E, D, NW, BC, false, false>;

@@ -1,5 +1,5 @@
 // Software-pipelined forward attention kernel for gfx950 (16-bit inputs,
-// no causal mask, no additive mask).
+// optional causal mask, no additive mask).
 //
 // Same arithmetic as FwdKernel in attn_fwd_kernel.h -- the tiled online
 // softmax of "FlashAttention技术解析：优化Transformer注意力计算效率"
@@ -29,9 +29,14 @@
 // end of the block as one serial chain).  LDS fragments are read two steps
 // ahead of their MFMA.
 //
-// Tiles that reach past the key range (kv_lens, ragged Nk) are masked after
-// the main block and their maximum recomputed; the lazy rescale (reference
-// point moved only when a tile's maximum exceeds it by more than TH) follows.
+// Tiles that reach past the key range (kv_lens, ragged Nk) or, under the
+// causal mask, past some row's own position (key i visible to query rows
+// >= i) are masked after the main block and their maximum recomputed; the
+// lazy rescale (reference point moved only when a tile's maximum exceeds it
+// by more than TH) follows.  Causal work-groups stop at the tile holding
+// their last row's key; the waves with earlier rows run the remaining tiles
+// fully masked (exponentials of -inf are 0), which keeps every wave in the
+// shared loads and barriers.
 #pragma once
 
 #include "attn_kernels.h"
@@ -39,7 +44,7 @@
 
 namespace attn {
 
-template <class E, int D, int BC>
+template <class E, int D, int BC, bool CAUSAL>
 struct FwdPipeKernel {
   static constexpr float TH = 8.0f;                 // rescale threshold, log2 units
   static constexpr int NW = 8;                      // waves per work-group
@@ -135,16 +140,18 @@ struct FwdPipeKernel {
   }
 
   static __device__ __forceinline__ bool is_edge(const State& st, int j) {
-    return j * BC + BC > st.kv_limit;
+    return j * BC + BC > st.kv_limit || (CAUSAL && j * BC + BC - 1 > st.q_w0);
   }
   static __device__ __forceinline__ void mask_edge(const State& st, Scores& s, int j) {
     const int j0 = j * BC;
+    // keys >= lim are excluded for this lane's query row q_w0 + l32
+    const int lim = CAUSAL ? min(st.kv_limit, st.q_w0 + st.l32 + 1) : st.kv_limit;
 #pragma unroll
     for (int k = 0; k < KB; ++k)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = j0 + k * 32 + (e >> 2) * 8 + st.hl * 4 + (e & 3);
-        if (key >= st.kv_limit) s[k][e] = -INFINITY;
+        if (key >= lim) s[k][e] = -INFINITY;
       }
   }
   static __device__ __forceinline__ float row_max(const Scores& s) {
@@ -294,7 +301,8 @@ struct FwdPipeKernel {
     st.l32 = st.lane & 31;
 
     const int wid = xcd_remap(blockIdx.x, a.total_blocks);
-    const int qblk = wid % a.nqb;
+    int qblk = wid % a.nqb;
+    if (CAUSAL) qblk = a.nqb - 1 - qblk;  // longest rows first
     const int bh = wid / a.nqb;
     const int h = bh % a.Hq;
     const int b = bh / a.Hq;
@@ -303,7 +311,9 @@ struct FwdPipeKernel {
 
     st.kv_limit = a.Nk;
     if (a.kv_lens) st.kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
-    st.n_act = (st.kv_limit + BC - 1) / BC;
+    int kv_end = st.kv_limit;
+    if (CAUSAL) kv_end = min(kv_end, min(qblk * ROWS + ROWS, a.Nq));
+    st.n_act = (kv_end + BC - 1) / BC;
     const int n_tiles = st.n_act;
     const int dchunks = a.d / 8;
     st.c = a.c;
@@ -392,10 +402,10 @@ struct FwdPipeKernel {
   }
 };
 
-template <class E, int D, int BC>
+template <class E, int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pipe_kernel(FwdArgs a) {
-  using K = FwdPipeKernel<E, D, BC>;
+  using K = FwdPipeKernel<E, D, BC, CAUSAL>;
   __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];

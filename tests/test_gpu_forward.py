@@ -132,6 +132,32 @@ def test_forward_stage_rotation(gpu_lib, case):
     check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
 
 
+# Causal calls whose work-groups see >= 8 key tiles (min(Nq, Nk) >= 512) take
+# the software-pipelined kernel: diagonal tiles masked per row, the tile
+# count capped at each block's last row, ragged last blocks, key lengths
+# below and above the diagonal, GQA, both layouts, a padded head dimension
+# (query i sees keys <= i; causal calls have Nq = Nk).
+PIPE_CAUSAL = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, lens, layout
+    ("pipe_causal_d128", 1, 4, 4, 600, 600, 128, "bf16", None, "bhnd"),
+    ("pipe_causal_gqa_lens_d128", 2, 8, 2, 700, 700, 128, "bf16", (100, 700), "bhnd"),
+    ("pipe_causal_fp16_d64_bnhd", 1, 2, 1, 520, 520, 64, "fp16", None, "bnhd"),
+    ("pipe_causal_lens_d96", 2, 2, 2, 900, 900, 96, "bf16", (530, 900), "bhnd"),
+    ("pipe_causal_fp16_d128_bnhd", 1, 2, 1, 1000, 1000, 128, "fp16", None, "bnhd"),
+]
+
+
+@pytest.mark.parametrize("case", PIPE_CAUSAL, ids=[c[0] for c in PIPE_CAUSAL])
+def test_forward_pipelined_causal(gpu_lib, case):
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, lens, layout = case
+    _say(f"[fwd-pipe-causal] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens)
+    o, lse = _run(w, x, layout=layout, causal=True)
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], causal=True, kv_lens=x["kv_lens"])
+    check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
+
+
 def test_forward_empty_and_no_keys(gpu_lib):
     import torch
     from exact_attention_25_amd import binding as bd
