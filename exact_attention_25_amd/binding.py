@@ -9,7 +9,6 @@ there is no fallback path.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -349,7 +348,3 @@ def attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, *, layout="bhnd", causa
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8")
     return out, lse
-
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)

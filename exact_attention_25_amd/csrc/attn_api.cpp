@@ -155,9 +155,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: D [B,Hq,ld] | nl2 [B,Hq,ld] | (kv_chunks > 1) partial
 // dK and dV, [kv_chunks, B, Hkv, Nk, d] fp32 each | (bf16 inputs) fp16
-// copies of q, dout and k in their own layout; ld = Nq rounded up to 128.
+// copies of q, dout and k in their own layout, then the pre-pass maxima
+// [kBwdAmaxBlocks][4] and the 4 operand scales; ld = Nq rounded up to 128.
 struct BwdWorkspace {
-  size_t rows, part, cq, ck, total;
+  size_t rows, part, cq, ck, amax, total;
   int chunks, ld;
 };
 
@@ -172,7 +173,8 @@ BwdWorkspace bwd_workspace(const attn_params* p) {
   const bool cvt = p->dtype == ATTN_BF16;
   w.cq = cvt ? align256((size_t)p->B * p->Hq * p->Nq * p->d * 2) : 0;
   w.ck = cvt ? align256((size_t)p->B * p->Hkv * p->Nk * p->d * 2) : 0;
-  w.total = 2 * w.rows + 2 * w.part + 2 * w.cq + w.ck;
+  w.amax = cvt ? align256((size_t)attn::kBwdAmaxBlocks * 4 * sizeof(float)) + 256 : 0;
+  w.total = 2 * w.rows + 2 * w.part + 2 * w.cq + w.ck + w.amax;
   return w;
 }
 
@@ -216,6 +218,8 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
     a.q16 = c;
     a.do16 = c + ws.cq;
     a.k16 = c + 2 * ws.cq;
+    a.amax_part = reinterpret_cast<float*>(c + 2 * ws.cq + ws.ck);
+    a.escale = reinterpret_cast<float*>(c + 2 * ws.cq + ws.ck + ws.amax - 256);
   } else {
     a.q16 = q;
     a.do16 = dout;

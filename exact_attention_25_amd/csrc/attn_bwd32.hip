@@ -120,9 +120,11 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < BC * D; idx += NW * 64) {
       const int r = idx / D, c = idx % D;
+      // rows past kv_lens are zero, whatever the tensors hold there
       const int64_t grow = min(j0 + r, a.Nk - 1);
-      ks_[r * LD + c] = c < a.d ? kp[grow * a.k_sn + c] : 0.f;
-      vs_[r * LD + c] = c < a.d ? vp[grow * a.k_sn + c] : 0.f;
+      const bool ok = c < a.d && j0 + r < kv_limit;
+      ks_[r * LD + c] = ok ? kp[grow * a.k_sn + c] : 0.f;
+      vs_[r * LD + c] = ok ? vp[grow * a.k_sn + c] : 0.f;
     }
     __syncthreads();
     uint32_t w = 0;   // LOCAL: bit 8 (r / 4) + r % 4 set iff register r's key is visible

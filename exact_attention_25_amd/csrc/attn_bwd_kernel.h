@@ -77,6 +77,61 @@ __device__ __forceinline__ f16x8 to_f16x8(typename E::V8 x) {
   }
 }
 
+// Power-of-two scales of the fp16 operands of a bf16 backward.  The fp16
+// copies hold sq Q, sk K, sdo dO and (in registers) sv V, each scale chosen
+// from the tensor's largest magnitude so that the copy is exact and the
+// products that are rounded to fp16 stay in its range:
+//   S' = sq sk S          -> the exponent takes c / (sq sk);
+//   dP' = sdo sv dP       -> X = P dP' and dS' = P (dP' - D') stay below
+//                            128 * 8 * 8 = 8192 for d <= 128;
+//   dQ = scale / (sk sdo sv) (A' - D' B'),  dK = scale / (sdo sv sq) dK',
+//   dV = dV' / sdo.
+// Scaling by powers of two is exact, so inputs already in range (scale 1)
+// give the unscaled results bit for bit.  fp16 inputs use every scale = 1.
+struct BwdScales {
+  float q, k, v, dout;
+};
+__device__ __forceinline__ BwdScales bwd_scales(const BwdArgs& a) {
+  if (!a.escale) return {1.f, 1.f, 1.f, 1.f};
+  return {a.escale[0], a.escale[1], a.escale[2], a.escale[3]};
+}
+
+// 2^(target - t) for a tensor whose largest magnitude amax has binary
+// exponent t outside [lo, hi] (1 inside it, or for a zero / non-finite
+// amax); the exponent shift is clamped to +-40 so that products of three
+// scales stay normal fp32 numbers.
+__device__ __forceinline__ float pow2_scale(float amax, int lo, int hi, int target) {
+  if (!(amax > 0.f) || !(amax < INFINITY)) return 1.f;
+  const int t = __builtin_amdgcn_frexp_expf(amax) - 1;   // amax in [2^t, 2^(t+1))
+  if (t >= lo && t <= hi) return 1.f;
+  return __builtin_amdgcn_ldexpf(1.f, max(-40, min(40, target - t)));
+}
+// Q and K: largest magnitude kept in [2^-6, 2^14), else moved to [2^13, 2^14);
+// dO and V: kept in [2^-6, 8), else moved to [4, 8).
+constexpr int kQkLo = -6, kQkHi = 13, kQkTarget = 13;
+constexpr int kDvLo = -6, kDvHi = 2, kDvTarget = 2;
+
+// 8 x 16-bit input values times a power of two -> 8 x fp16.
+template <class E>
+__device__ __forceinline__ f16x8 to_f16x8_scaled(typename E::V8 x, float s) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  if constexpr (std::is_same<E, FP16>::value) {
+    return x;
+  } else {
+    return __builtin_convertvector(__builtin_convertvector(x, f32x8) * s, f16x8);
+  }
+}
+// 8 x bf16 values times a power of two, still bf16 (exact); fp16 unchanged.
+template <class E>
+__device__ __forceinline__ typename E::V8 scale_v8(typename E::V8 x, float s) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  if constexpr (std::is_same<E, FP16>::value) {
+    return x;
+  } else {
+    return __builtin_convertvector(__builtin_convertvector(x, f32x8) * s, typename E::V8);
+  }
+}
+
 // A tile of R rows x D columns (16-bit) in LDS, loaded by NW waves.
 template <int R, int D, int NW>
 struct PadTile {
@@ -237,6 +292,7 @@ struct BwdQ {
     int t_lo, t_hi;             // LOCAL: this wave's key tiles [t_lo, t_hi)
     LocalVis::Row lrow;         // LOCAL: this lane's query position
     float cap_a, cap_c2;        // SOFTCAP constants
+    float dq_scale;             // scale / (sk sdo sv)
     H8 qf[KS];
     V8 df[KS];
     f32x16 acc_a[DT], acc_b[DT];
@@ -493,23 +549,25 @@ struct BwdQ {
     const int n_act = CAUSAL ? min(n_tiles, (st.q_w0 + 31) / BC + 1) : n_tiles;
 
     const int crow = min(st.qrow, a.Nq - 1);
+    const BwdScales sc = bwd_scales(a);
     {
       const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh + crow * a.q_sn;
       const T* dp = (const T*)a.dout + b * a.q_sb + h * a.q_sh + crow * a.q_sn;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int d0 = ks * 16 + st.hl * 8;
-        st.qf[ks] = d0 < a.d ? to_f16x8<E>(*(const V8*)(qp + d0)) : H8{};
-        st.df[ks] = d0 < a.d ? *(const V8*)(dp + d0) : V8{};
+        st.qf[ks] = d0 < a.d ? to_f16x8_scaled<E>(*(const V8*)(qp + d0), sc.q) : H8{};
+        st.df[ks] = d0 < a.d ? scale_v8<E>(*(const V8*)(dp + d0), sc.dout * sc.v) : V8{};
       }
     }
     const float lse = a.lse[((int64_t)b * a.Hq + h) * a.Nq + crow];
     st.nl2 = (st.qrow < a.Nq && lse != -INFINITY) ? -lse * kLog2e : -INFINITY;
     st.nk1 = a.Nk - 1;
     if (MASK) st.mrow = a.mask + b * a.m_sb + h * a.m_sh + (int64_t)crow * a.m_sq;
-    st.c = a.c;
+    st.c = a.c / (sc.q * sc.k);
     st.cap_a = a.cap_a;
-    st.cap_c2 = a.cap_c2;
+    st.cap_c2 = a.cap_c2 / (sc.q * sc.k);
+    st.dq_scale = a.scale / (sc.k * sc.dout * sc.v);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       st.acc_a[dt] = f32x16{};
@@ -521,7 +579,9 @@ struct BwdQ {
     st.kp = (const char*)((const _Float16*)a.k16 + b * a.k_sb + g * a.k_sh);
     st.vp = (const char*)((const T*)a.v + b * a.k_sb + g * a.k_sh);
     st.tile_bytes = (int64_t)BC * a.k_sn * 2;
-    st.end_bytes = ((int64_t)(a.Nk - 1) * a.k_sn + a.d) * 2;
+    // rows past kv_lens read as zero: S = -inf there and dP = 0, whatever
+    // those rows hold
+    st.end_bytes = max(((int64_t)(st.kv_limit - 1) * a.k_sn + a.d) * 2, (int64_t)0);
     const int dchunks = a.d / 8;
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i)
@@ -569,7 +629,7 @@ struct BwdQ {
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          x[e] = a.scale * (st.acc_a[dt][gq * 4 + e] - dtot * st.acc_b[dt][gq * 4 + e]);
+          x[e] = st.dq_scale * (st.acc_a[dt][gq * 4 + e] - dtot * st.acc_b[dt][gq * 4 + e]);
         if (a.grad_f32) {
           f32x4 w = {x[0], x[1], x[2], x[3]};
           *(f32x4*)((float*)a.dq + base + col) = w;
@@ -908,6 +968,7 @@ struct BwdKV {
     if (a.kv_lens) st.kv_limit = min(max(a.kv_lens[b], 0), a.Nk);
 
     // K^T and V^T fragments of this lane's key, fp16 (zero beyond d)
+    const BwdScales sc = bwd_scales(a);
     {
       const int krow = min(st.key, a.Nk - 1);
       const T* kp = (const T*)a.k + b * a.k_sb + g * a.k_sh + krow * a.k_sn;
@@ -915,8 +976,8 @@ struct BwdKV {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int d0 = ks * 16 + st.hl * 8;
-        st.kf[ks] = d0 < a.d ? to_f16x8<E>(*(const V8*)(kp + d0)) : H8{};
-        st.vf[ks] = d0 < a.d ? to_f16x8<E>(*(const V8*)(vp + d0)) : H8{};
+        st.kf[ks] = d0 < a.d ? to_f16x8_scaled<E>(*(const V8*)(kp + d0), sc.k) : H8{};
+        st.vf[ks] = d0 < a.d ? to_f16x8_scaled<E>(*(const V8*)(vp + d0), sc.v) : H8{};
       }
     }
 #pragma unroll
@@ -924,9 +985,10 @@ struct BwdKV {
       st.dk[dt] = f32x16{};
       st.dv[dt] = f32x16{};
     }
-    st.c = a.c;
+    st.c = a.c / (sc.q * sc.k);
     st.cap_a = a.cap_a;
-    st.cap_c2 = a.cap_c2;
+    st.cap_c2 = a.cap_c2 / (sc.q * sc.k);
+    const float dk_scale = a.scale / (sc.dout * sc.v * sc.q), dv_scale = 1.f / sc.dout;
     st.nq1 = a.Nq - 1;
     st.q0p = (const char*)((const _Float16*)a.q16 + b * a.q_sb);
     st.d0p = (const char*)((const _Float16*)a.do16 + b * a.q_sb);
@@ -998,8 +1060,8 @@ struct BwdKV {
         if (kr >= a.Nk) continue;
         const int64_t off = b * a.k_sb + g * a.k_sh + kr * a.k_sn + col;
         const bool kv_ok = kr < st.kv_limit;
-        const float kval = kv_ok ? st.dk[dt][r] * a.scale : 0.f;
-        const float vval = kv_ok ? st.dv[dt][r] : 0.f;
+        const float kval = kv_ok ? st.dk[dt][r] * dk_scale : 0.f;
+        const float vval = kv_ok ? st.dv[dt][r] * dv_scale : 0.f;
         if (!direct) {
           a.part_dk[chunk * part + off] = kval;
           a.part_dv[chunk * part + off] = vval;

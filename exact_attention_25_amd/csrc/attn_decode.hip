@@ -74,8 +74,8 @@ struct DecodeSplit {
     return (uint32_t)((r * sn + ch * 8) * 2);
   }
 
-  // K and V rows key_lo + jr .. +31 (rows past Nk read as zero); jr is a
-  // multiple of BC
+  // K and V rows key_lo + jr .. +31 (rows past the valid length read as
+  // zero); jr is a multiple of BC
   static __device__ __forceinline__ void issue(const State& st, int jr, char* kb, char* vb) {
     // the buffer may have just been read by this wave: its LDS reads finish first
     __builtin_amdgcn_s_waitcnt(kLdsOnly);
@@ -192,9 +192,10 @@ struct DecodeSplit {
     st.kp = (const char*)((const T*)a.k + b * a.k_sb + g * a.k_sh + (int64_t)key_lo * a.k_sn);
     st.vp = (const char*)((const T*)a.v + b * a.k_sb + g * a.k_sh + (int64_t)key_lo * a.k_sn);
     st.tile_bytes = (int64_t)BC * a.k_sn * 2;
-    // bytes from key key_lo to the end of key Nk-1 (used only when n_tiles > 0,
-    // i.e. key_lo < Nk)
-    st.k_end = ((int64_t)(a.Nk - 1 - key_lo) * a.k_sn + a.d) * 2;
+    // bytes from key key_lo to the end of the last valid key kv_limit-1 (used
+    // only when n_tiles > 0, i.e. key_lo < kv_limit): cache rows past the
+    // valid length read as zero, whatever they hold
+    st.k_end = ((int64_t)(kv_limit - 1 - key_lo) * a.k_sn + a.d) * 2;
     const int dchunks = a.d / 8;
 #pragma unroll
     for (int i = 0; i < K_INS; ++i) st.koff[i] = dma_offset(i, lane, KPS, dchunks, a.k_sn);

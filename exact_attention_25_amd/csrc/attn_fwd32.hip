@@ -84,9 +84,11 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < BC * D; idx += NW * 64) {
       const int r = idx / D, c = idx % D;
+      // rows past kv_lens are zero, whatever the tensors hold there
       const int grow = min(j0 + r, a.Nk - 1);
-      ks_[r * LD + c] = c < a.d ? kp[grow * a.k_sn + c] : 0.f;
-      vs_[r * LD + c] = c < a.d ? vp[grow * a.v_sn + c] : 0.f;
+      const bool ok = c < a.d && j0 + r < kv_limit;
+      ks_[r * LD + c] = ok ? kp[grow * a.k_sn + c] : 0.f;
+      vs_[r * LD + c] = ok ? vp[grow * a.v_sn + c] : 0.f;
     }
     __syncthreads();
     uint32_t bits = 0;   // LOCAL: bit i set iff key j0 + i is visible to this lane's row

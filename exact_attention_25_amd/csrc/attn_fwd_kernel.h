@@ -104,7 +104,7 @@ struct FwdKernel {
     const char* kp;             // K / V of this (batch, kv-head), key 0
     const char* vp;
     int64_t k_tile, v_tile;     // bytes between consecutive tiles
-    int64_t k_end, v_end;       // bytes from kp / vp to the end of key nk-1
+    int64_t k_end, v_end;       // bytes from kp / vp to the end of key kv_limit-1
     // per DMA instruction of this lane: byte offset (within a tile) of the
     // chunk it copies, kBufOutOfRange for pad slots and columns past d
     uint32_t koff[K_IPW], voff[V_IPW];
@@ -126,8 +126,8 @@ struct FwdKernel {
   }
 
   // Direct loads of one K tile and one V tile (keys j0..j0+BC-1), through
-  // buffer resources that end at key nk-1: rows past it, pad slots and
-  // columns past d read as zero.  Keys past the end are masked to -inf and
+  // buffer resources that end at the last valid key (kv_limit-1): rows past
+  // it, pad slots and columns past d read as zero.  Keys past the end are masked to -inf and
   // zero K columns meet zero Q columns, so none of them reach the result.
   static __device__ __forceinline__ void issue(const State& st, int j0, char* kb, char* vb) {
     const int64_t ko = (int64_t)(j0 / BC) * st.k_tile, vo = (int64_t)(j0 / BC) * st.v_tile;
@@ -367,8 +367,9 @@ struct FwdKernel {
     st.vp = (const char*)((const T*)a.v + b * a.v_sb + g * a.v_sh);
     st.k_tile = (int64_t)BC * a.k_sn * 2;
     st.v_tile = (int64_t)BC * a.v_sn * 2;
-    st.k_end = ((int64_t)(a.Nk - 1) * a.k_sn + a.d) * 2;
-    st.v_end = ((int64_t)(a.Nk - 1) * a.v_sn + a.d) * 2;
+    // rows past kv_lens read as zero (their contents never reach O)
+    st.k_end = max(((int64_t)(st.kv_limit - 1) * a.k_sn + a.d) * 2, (int64_t)0);
+    st.v_end = max(((int64_t)(st.kv_limit - 1) * a.v_sn + a.d) * 2, (int64_t)0);
 #pragma unroll
     for (int i = 0; i < K_IPW; ++i)
       st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn);

@@ -87,7 +87,7 @@ struct FwdPipeKernel {
     const char* kp;             // K / V of this (batch, kv-head), key 0
     const char* vp;
     int64_t k_tile, v_tile;     // bytes between consecutive tiles
-    int64_t k_end, v_end;       // bytes from kp / vp to the end of key Nk-1
+    int64_t k_end, v_end;       // bytes from kp / vp to the end of key kv_limit-1
     uint32_t koff[K_IPW], voff[V_IPW];  // per load instruction: byte offset in a tile
     int kbase, vbase;           // per-lane LDS byte offsets of the read patterns
     float c;                    // scale * log2(e)
@@ -321,8 +321,11 @@ struct FwdPipeKernel {
     st.vp = (const char*)((const T*)a.v + b * a.v_sb + g * a.v_sh);
     st.k_tile = (int64_t)BC * a.k_sn * 2;
     st.v_tile = (int64_t)BC * a.v_sn * 2;
-    st.k_end = ((int64_t)(a.Nk - 1) * a.k_sn + a.d) * 2;
-    st.v_end = ((int64_t)(a.Nk - 1) * a.v_sn + a.d) * 2;
+    // the resources end at the last valid key: rows past kv_lens (which may
+    // hold anything, e.g. an unwritten cache tail) read as zero, so that
+    // their P = 0 never meets a NaN or an infinity
+    st.k_end = max(((int64_t)(st.kv_limit - 1) * a.k_sn + a.d) * 2, (int64_t)0);
+    st.v_end = max(((int64_t)(st.kv_limit - 1) * a.v_sn + a.d) * 2, (int64_t)0);
 #pragma unroll
     for (int i = 0; i < K_IPW; ++i)
       st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn);

@@ -45,6 +45,12 @@ struct BwdArgs {
   const void* q16;
   const void* do16;
   const void* k16;
+  // bf16 inputs: per-block largest magnitudes of q, k, v, dout
+  // ([amax_blocks][4]) and the power-of-two operand scales derived from them
+  // (sq, sk, sv, sdo; see BwdScales); null for fp16 inputs (all scales 1)
+  float* amax_part;
+  float* escale;
+  int32_t amax_blocks;
   void* dq;
   void* dk;
   void* dv;
@@ -147,6 +153,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, bool softcap, hipStr
 
 // Work split of the backward, shared by the workspace sizing and the launch.
 constexpr int kBwdKeysPerBlock = 128;   // keys per dK/dV work-group
+constexpr int kBwdAmaxBlocks = 2048;    // work-groups of the bf16 -> fp16 pre-pass
 int bwd_kv_chunks(int B, int Hkv, int Nk, int group);
 
 // Variant switches of a forward launch.

@@ -86,7 +86,10 @@ typedef struct {
   const float* mask;
   int64_t mask_sb, mask_sh, mask_sq;
   /* Optional [B] int32 valid key counts: keys j >= kv_lens[b] are excluded.
-   * Values are clamped to [0, Nk].  NULL = all Nk keys are valid. */
+   * Values are clamped to [0, Nk].  NULL = all Nk keys are valid.  The rows
+   * of k and v past kv_lens[b] are never read into a result (they may hold
+   * anything, NaN and infinities included), except by attn_quantize_fp8,
+   * whose 64-row block scales span them. */
   const int32_t* kv_lens;
   /* Local attention and the soft cap; a zero-filled tail means none of them.
    * Query row i sits at position p = i in attn_fwd / attn_bwd and at
@@ -139,7 +142,7 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
  * [B, Hq, Nq rounded up to 128] float arrays (D and -LSE*log2(e)); for
  * 16-bit inputs whose q-heads of a kv-head are split over several
  * work-groups, fp32 partial dK and dV sums; for bf16 inputs, fp16 copies of
- * q, dout and k. */
+ * q, dout and k, and 32 KB of per-block maxima and scales. */
 size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /* Backward pass: gradients of <dout, O> with O = attention(q, k, v), with the
@@ -158,7 +161,12 @@ size_t attn_bwd_workspace_bytes(const attn_params* p);
  * causal, the window, the grid and the soft cap (whose derivative
  * 1 - tanh^2(s / softcap) multiplies dS) and all three dtypes are supported
  * (fp32 inputs take an all-fp32 path).  The result is deterministic: no
- * atomics. */
+ * atomics.  bf16 inputs run the products that take P or dS on fp16 operands
+ * (11-bit significands, the precision the 2e-2 tolerance of the causal GQA
+ * case needs); the fp16 copies of q, k, v and dout are scaled by powers of
+ * two found on the device from each tensor's largest magnitude and the
+ * scales are undone exactly, so bf16 inputs above 65504 or below 2^-14 are
+ * handled (fully for largest magnitudes within [2^-27, 2^42]). */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,

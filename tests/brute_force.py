@@ -11,10 +11,11 @@ import math
 
 
 def attention(q, k, v, scale, causal=False, mask=None, kv_len=None, softcap=None,
-              window=None, grid=None, last_positions=False):
+              window=None, grid=None, last_positions=False, with_probs=False):
     """q: list of Nq rows, k/v: lists of Nk rows (lists of floats).
 
-    Returns (o rows, lse list).  mask: Nq x Nk list or None.
+    Returns (o rows, lse list), and with ``with_probs`` also the Nq x Nk
+    softmax weights p_ij.  mask: Nq x Nk list or None.
 
     Local options: the query of row i sits at position p = i, or with
     ``last_positions`` at the (L - Nq + i)-th of the L valid keys.  softcap:
@@ -26,7 +27,7 @@ def attention(q, k, v, scale, causal=False, mask=None, kv_len=None, softcap=None
     """
     nq, nk, d = len(q), len(k), len(q[0])
     L = nk if kv_len is None else kv_len
-    out, lses = [], []
+    out, lses, probs = [], [], []
     for i in range(nq):
         p = (L - nq + i) if last_positions else i
         logits = []
@@ -63,6 +64,7 @@ def attention(q, k, v, scale, causal=False, mask=None, kv_len=None, softcap=None
         if not vis:
             out.append([0.0] * d)
             lses.append(-math.inf)
+            probs.append([0.0] * nk)
             continue
         big = max(vis)
         w = [0.0 if (x is None or x == -math.inf) else math.exp(x - big) for x in logits]
@@ -75,4 +77,7 @@ def attention(q, k, v, scale, causal=False, mask=None, kv_len=None, softcap=None
             row.append(acc / tot)
         out.append(row)
         lses.append(big + math.log(tot))
+        probs.append([x / tot for x in w])
+    if with_probs:
+        return out, lses, probs
     return out, lses

@@ -3,8 +3,8 @@
 Small cases span several tiles with ragged tails in both sequence axes and
 cover every feature (dtypes, head dims incl. padded ones, layouts, causal,
 key padding, additive masks, GQA, empty and fully masked rows).  The
-full-size workloads are checked on sampled rows (the oracle computes rows
-independently) and by properties that hold at any size.
+full-size workloads are checked on every row of every head (the oracle
+computes rows independently, in slabs, on a pool of threads).
 """
 import sys
 import zlib
@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 
 from exact_attention_25_amd import inputs
-from oracle import ref_fwd, ref_fwd_rows
-from tests.gpu_util import check_out, from_layout, host, make_case, to_device, to_layout
+from oracle import ref_fwd
+from tests.gpu_util import (TOL_O, TOL_O_REL_RMS, check_out, from_layout, host, make_case,
+                            to_device, to_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -195,83 +196,67 @@ def test_forward_causal_row0_is_v0(gpu_lib):
 
 
 # ------------------------------------------------------- full-size workloads
-def _sample_rows(Nq, rng, n=24):
-    rows = set(rng.choice(Nq, size=min(n, Nq), replace=False).tolist())
-    rows.update({0, Nq - 1, max(Nq // 2, 0)})
-    return sorted(rows)
-
-
-def _hull_check(o, v, group):
-    """Each output row is a convex combination of V rows: inside their range."""
-    import torch
-    vv = v.float()
-    lo = vv.amin(dim=2).repeat_interleave(group, dim=1)
-    hi = vv.amax(dim=2).repeat_interleave(group, dim=1)
-    of = o.float()
-    slack = 1e-2 * (hi - lo).abs() + 1e-2
-    assert torch.all(of >= lo[:, :, None, :] - slack[:, :, None, :])
-    assert torch.all(of <= hi[:, :, None, :] + slack[:, :, None, :])
-
-
-def _workload_check(name, full_heads=False, n_heads=6, n_rows=24):
-    w = inputs.WORKLOADS[name]
-    _say(f"[fwd-workload] {name}: generating inputs")
+# Every row of every head of each workload is compared with the oracle
+# (tests/full_size.py), element by element, with the same bars as the small
+# cases; the error statistics are printed for the design notes' table.
+def _full_check(w, batches=None):
+    from tests.full_size import forward_all_rows
+    _say(f"[fwd-workload] {w.name}: generating inputs")
     x = inputs.make_inputs(w, with_do=False)
-    _say(f"[fwd-workload] {name}: running GPU")
+    _say(f"[fwd-workload] {w.name}: running GPU")
     o, lse = _run(w, x, causal=w.causal)
-    if full_heads:
-        _say(f"[fwd-workload] {name}: oracle over all heads")
-        O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], causal=w.causal, kv_lens=x["kv_lens"])
-        check_out(o, lse, O_ref, L_ref, w.dtype, name)
-        return w, x, o, lse
-    rng = np.random.default_rng(123)
-    oh, lh = host(o), host(lse)
-    heads = [(0, 0), (w.B - 1, w.Hq - 1)] + [
-        (int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n_heads - 2)]
-    import torch
-    for (b, h) in heads:
-        rows = _sample_rows(w.Nq, rng, n_rows)
-        O_ref, L_ref = ref_fwd_rows(x["q"], x["k"], x["v"], b, h, rows, causal=w.causal,
-                                    kv_lens=x["kv_lens"])
-        check_out(oh[b, h, rows], lh[b, h, rows], O_ref, L_ref, w.dtype, f"{name} b{b} h{h}")
-    _say(f"[fwd-workload] {name}: hull property over all rows")
-    v = to_device(x["v_raw"], w.dtype)
-    if x["kv_lens"] is None:
-        _hull_check(o, v, w.Hq // w.Hkv)
-    assert bool(torch.isfinite(lse).all())
+    oh = o.float().cpu().numpy()
+    lh = lse.cpu().numpy()
+    _say(f"[fwd-workload] {w.name}: oracle over every row"
+         + ("" if batches is None else f" of batches {list(batches)}"))
+    st, lerr, lmax, mism, secs = forward_all_rows(w, x, oh, lh, batches=batches)
+    _say(f"[fwd-workload] {w.name}: O max-abs {st.max_abs:.3e} rel-rms {st.rel_rms:.3e}, "
+         f"LSE max-abs {lerr:.3e}, rows {st.n // w.d}, oracle {secs:.1f} s")
+    assert st.finite, f"{w.name}: non-finite output"
+    assert st.n == len(batches or range(w.B)) * w.Hq * w.Nq * w.d
+    assert st.max_abs <= TOL_O[w.dtype], f"{w.name}: O max-abs {st.max_abs:.3e}"
+    assert st.rel_rms <= TOL_O_REL_RMS[w.dtype], f"{w.name}: O rel-rms {st.rel_rms:.3e}"
+    assert mism == 0, f"{w.name}: {mism} rows disagree on a fully masked (-inf) LSE"
+    ltol = (1e-5 if w.dtype == "fp32" else 1e-4) + 1e-6 * lmax
+    assert lerr <= ltol, f"{w.name}: LSE max-abs {lerr:.3e}"
     return w, x, o, lse
 
 
 def test_workload_tiny_fp32(gpu_lib):
-    _workload_check("tiny_fp32_b1_h2_n128_d64", full_heads=True)
+    _full_check(inputs.WORKLOADS["tiny_fp32_b1_h2_n128_d64"])
 
 
 def test_workload_vit_bf16(gpu_lib):
-    _workload_check("vit_bf16_b128_h16_n196_d64", full_heads=True)
+    _full_check(inputs.WORKLOADS["vit_bf16_b128_h16_n196_d64"])
 
 
 def test_workload_unet_cross_fp16(gpu_lib):
-    _workload_check("unet_cross_fp16_b2_h8_q4096_k77_d40", full_heads=True)
+    _full_check(inputs.WORKLOADS["unet_cross_fp16_b2_h8_q4096_k77_d40"])
 
 
 def test_workload_unet_self_fp16(gpu_lib):
-    _workload_check("unet_self_fp16_b2_h8_n4096_d40", n_heads=8, n_rows=48)
+    _full_check(inputs.WORKLOADS["unet_self_fp16_b2_h8_n4096_d40"])
 
 
 def test_workload_long_bf16(gpu_lib):
-    _workload_check("long_bf16_b8_h32_n4096_d128", n_heads=8, n_rows=32)
+    _full_check(inputs.WORKLOADS["long_bf16_b8_h32_n4096_d128"])
 
 
-def test_workload_causal_gqa_forward(gpu_lib):
+@pytest.mark.parametrize("part", [0, 1])
+def test_workload_causal_gqa_forward(gpu_lib, part):
     import torch
-    w, x, o, lse = _workload_check("causal_gqa_bf16_b4_h32_kv2_n8192_d128", n_heads=6, n_rows=32)
+    w = inputs.WORKLOADS["causal_gqa_bf16_b4_h32_kv2_n8192_d128"]
+    w, x, o, lse = _full_check(w, batches=range(2 * part, 2 * part + 2))
     v = to_device(x["v_raw"], w.dtype)
     G = w.Hq // w.Hkv
     assert torch.equal(o[:, :, 0], v[:, :, 0].repeat_interleave(G, dim=1))
 
 
-@pytest.mark.parametrize("n", [1024, 16384])
-def test_workload_long_sweep(gpu_lib, n):
-    w = inputs.sweep_workload(n)
-    inputs.WORKLOADS.setdefault(w.name, w)
-    _workload_check(w.name, n_heads=4, n_rows=16)
+# the long-context sweep (B * N = 32768); N = 16384 in two halves of the batch
+SWEEP = [(1024, None), (2048, None), (8192, None), (16384, (0,)), (16384, (1,))]
+
+
+@pytest.mark.parametrize("n,batches", SWEEP,
+                         ids=[f"n{n}" + ("" if b is None else f"_b{b[0]}") for n, b in SWEEP])
+def test_workload_long_sweep(gpu_lib, n, batches):
+    _full_check(inputs.sweep_workload(n), batches=batches)

@@ -14,8 +14,9 @@ import numpy as np
 import pytest
 
 from exact_attention_25_amd import inputs
-from oracle import ref_fwd, ref_fwd_rows
-from tests.gpu_util import check_out, from_layout, host, make_case, to_device, to_layout
+from oracle import ref_fwd
+from tests.gpu_util import (TOL_O, TOL_O_REL_RMS, check_out, from_layout, host, make_case,
+                            to_device, to_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,9 +168,11 @@ def test_local_decode(gpu_lib, case):
 
 
 # ------------------------------------------------------------- full workloads
-def _workload_rows(name, n_heads=6, n_rows=32):
+def _workload_rows(name):
+    """Every row of every head of a full-size workload against the oracle."""
     import torch
     from exact_attention_25_amd import binding as bd
+    from tests.full_size import forward_all_rows
     w = inputs.WORKLOADS[name]
     _say(f"[local-workload] {name}: inputs")
     x = inputs.make_inputs(w, with_do=False)
@@ -179,17 +182,16 @@ def _workload_rows(name, n_heads=6, n_rows=32):
     o, lse = bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["lens"],
                          window_size=w.window or (-1, -1), grid=w.grid, softcap=w.softcap)
     torch.cuda.synchronize()
-    oh, lh = host(o), host(lse)
-    rng = np.random.default_rng(5)
-    heads = [(0, 0), (w.B - 1, w.Hq - 1)] + [
-        (int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n_heads - 2)]
-    for (b, h) in heads:
-        rows = sorted(set(rng.choice(w.Nq, size=n_rows, replace=False).tolist())
-                      | {0, w.Nq - 1, w.Nq // 2})
-        O_ref, L_ref = ref_fwd_rows(x["q"], x["k"], x["v"], b, h, rows, causal=w.causal,
-                                    kv_lens=x["kv_lens"], **{k: v for k, v in opts.items() if v})
-        check_out(oh[b, h, rows], lh[b, h, rows], O_ref, L_ref, w.dtype, f"{name} b{b} h{h}")
-    assert bool(torch.isfinite(lse).all())
+    oh, lh = o.float().cpu().numpy(), lse.cpu().numpy()
+    _say(f"[local-workload] {name}: oracle over every row")
+    st, lerr, lmax, mism, secs = forward_all_rows(
+        w, x, oh, lh, mods={k: v for k, v in opts.items() if v})
+    _say(f"[local-workload] {name}: O max-abs {st.max_abs:.3e} rel-rms {st.rel_rms:.3e}, "
+         f"LSE max-abs {lerr:.3e}, oracle {secs:.1f} s")
+    assert st.finite and st.n == oh.size
+    assert st.max_abs <= TOL_O[w.dtype] and st.rel_rms <= TOL_O_REL_RMS[w.dtype]
+    assert mism == 0
+    assert lerr <= 1e-4 + 1e-6 * lmax, lerr
 
 
 def test_workload_vit_softcap(gpu_lib):

@@ -1,0 +1,120 @@
+"""Key/value rows past kv_lens are never read into a result.
+
+A cache or a padded batch may hold anything past a sequence's valid length
+(an unwritten tail, NaN, infinities).  The kernels exclude those keys
+(reading "key padding masks keys only" as exact exclusion), so the outputs
+with NaN / +inf / -inf in every K and V row past kv_lens must equal, bit for
+bit, the outputs with the finite seeded values there: O and LSE of the
+forward (every kernel family), the decode, and dQ, dK, dV of the backward
+(dK and dV are zero past kv_lens in both runs).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import make_case, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _poison(t, lens):
+    """Copy of K or V [B,H,N,d] with rows past lens[b] set to NaN / +inf / -inf."""
+    import torch
+    u = t.clone()
+    for b, L in enumerate(lens.tolist()):
+        tail = u[b, :, L:]
+        if tail.numel() == 0:
+            continue
+        tail[..., 0::3] = float("nan")
+        tail[..., 1::3] = float("inf")
+        tail[..., 2::3] = float("-inf")
+    return u
+
+
+def _inputs(case, with_do):
+    import torch
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens = case
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens, with_do=with_do)
+    t = {n: to_device(x[n + "_raw"], dtype) for n in (("q", "k", "v", "do") if with_do
+                                                       else ("q", "k", "v"))}
+    lens_d = torch.from_numpy(x["kv_lens"]).cuda()
+    return t, lens_d, x["kv_lens"]
+
+
+FWD = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens
+    ("fwd_tiles_bf16", 2, 4, 2, 200, 300, 128, "bf16", False, (100, 250)),
+    ("fwd_tiles_fp16_d64", 2, 2, 2, 130, 320, 64, "fp16", False, (70, 200)),
+    ("fwd_pipelined_bf16", 2, 4, 2, 300, 900, 128, "bf16", False, (530, 700)),
+    ("fwd_pipelined_causal_fp16", 2, 4, 2, 800, 800, 64, "fp16", True, (530, 700)),
+    ("fwd_fp32", 2, 2, 2, 100, 150, 64, "fp32", False, (60, 120)),
+]
+
+
+@pytest.mark.parametrize("case", FWD, ids=[c[0] for c in FWD])
+def test_forward_ignores_rows_past_kv_lens(gpu_lib, case):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    _say(f"[padding-fwd] {case[0]}")
+    t, lens_d, lens = _inputs(case, False)
+    causal = case[8]
+    o1, l1 = bd.attn_fwd(t["q"], t["k"], t["v"], causal=causal, kv_lens=lens_d)
+    o2, l2 = bd.attn_fwd(t["q"], _poison(t["k"], lens), _poison(t["v"], lens), causal=causal,
+                         kv_lens=lens_d)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o1).all())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_ignores_cache_past_kv_lens(gpu_lib):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    case = ("decode_bf16", 2, 8, 2, 2, 4000, 128, "bf16", True, (1000, 3000))
+    _say(f"[padding-decode] {case[0]}")
+    t, lens_d, lens = _inputs(case, False)
+    o1, l1 = bd.attn_decode(t["q"], t["k"], t["v"], causal=True, kv_lens=lens_d)
+    o2, l2 = bd.attn_decode(t["q"], _poison(t["k"], lens), _poison(t["v"], lens), causal=True,
+                            kv_lens=lens_d)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o1).all())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+BWD = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens
+    ("bwd_bf16_gqa", 2, 4, 2, 200, 300, 128, "bf16", False, (100, 250)),
+    ("bwd_fp16_causal_d64", 2, 4, 2, 260, 260, 64, "fp16", True, (90, 200)),
+    ("bwd_fp32", 2, 2, 1, 100, 150, 64, "fp32", False, (60, 120)),
+]
+
+
+@pytest.mark.parametrize("case", BWD, ids=[c[0] for c in BWD])
+def test_backward_ignores_rows_past_kv_lens(gpu_lib, case):
+    import torch
+    from exact_attention_25_amd import binding as bd
+    _say(f"[padding-bwd] {case[0]}")
+    t, lens_d, lens = _inputs(case, True)
+    causal = case[8]
+
+    def run(k, v):
+        o, lse = bd.attn_fwd(t["q"], k, v, causal=causal, kv_lens=lens_d)
+        return (o, lse) + tuple(bd.attn_bwd(t["q"], k, v, o, lse, t["do"], causal=causal,
+                                            kv_lens=lens_d))
+
+    r1 = run(t["k"], t["v"])
+    r2 = run(_poison(t["k"], lens), _poison(t["v"], lens))
+    torch.cuda.synchronize()
+    for n, a, b in zip(("o", "lse", "dq", "dk", "dv"), r1, r2):
+        assert torch.equal(a, b), n
+    dk = r1[3]
+    for b, L in enumerate(lens.tolist()):
+        assert bool((dk[b, :, L:] == 0).all()) and bool((r1[4][b, :, L:] == 0).all())
+    assert all(bool(torch.isfinite(x).all()) for x in r1[2:])

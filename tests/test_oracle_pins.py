@@ -168,6 +168,47 @@ def test_probability_rows_sum_to_one():
     assert np.all(np.triu(P[0, 0], 1) == 0.0)
 
 
+# ref_probs against the pure-Python weights: GQA head mapping (q-head h reads
+# kv-head h // G), a non-default scale, an additive mask with a -inf entry,
+# key lengths, causal rows and the BNHD layout; then P V equals ref_fwd's O.
+PROB_CASES = [
+    # B, Hq, Hkv, Nq, Nk, d, causal, use_mask, use_lens, layout, scale
+    (2, 4, 2, 5, 7, 3, False, True, True, "bhnd", 0.61),
+    (1, 6, 2, 6, 6, 4, True, False, False, "bnhd", None),
+    (2, 4, 1, 4, 9, 2, False, False, True, "bnhd", 1.7),
+]
+
+
+@pytest.mark.parametrize("case", PROB_CASES)
+def test_ref_probs_matches_brute_force(case):
+    B, Hq, Hkv, Nq, Nk, d, causal, use_mask, use_lens, layout, scale = case
+    q = _rand(B, Hq, Nq, d)
+    k = _rand(B, Hkv, Nk, d)
+    v = _rand(B, Hkv, Nk, d)
+    mask = _rand(B, Hq, Nq, Nk) if use_mask else None
+    if use_mask:
+        mask[1, 2, 1, 0] = -np.inf
+    lens = np.array([Nk - 2, 3][:B]) if use_lens else None
+    tr = (lambda x: x) if layout == "bhnd" else (lambda x: x.transpose(0, 2, 1, 3).copy())
+    P = ref_probs(tr(q), tr(k), scale=scale, causal=causal, mask=mask, kv_lens=lens,
+                  layout=layout)
+    assert P.shape == (B, Hq, Nq, Nk)
+    s = (1.0 / math.sqrt(d)) if scale is None else scale
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            _, _, pb = brute_force.attention(
+                q[b, h].tolist(), k[b, h // G].tolist(), v[b, h // G].tolist(), s,
+                causal=causal, mask=None if mask is None else mask[b, h].tolist(),
+                kv_len=None if lens is None else int(lens[b]), with_probs=True)
+            np.testing.assert_allclose(P[b, h], np.array(pb), rtol=0, atol=1e-13)
+    O, _ = ref_fwd(tr(q), tr(k), tr(v), scale=scale, causal=causal, mask=mask, kv_lens=lens,
+                   layout=layout)
+    O = O if layout == "bhnd" else O.transpose(0, 2, 1, 3)
+    vg = np.repeat(v, G, axis=1)
+    np.testing.assert_allclose(P @ vg, O, rtol=0, atol=1e-13)
+
+
 def test_permuting_keys_and_values_together():
     q, k, v = _rand(1, 2, 5, 4), _rand(1, 2, 8, 4), _rand(1, 2, 8, 4)
     perm = RNG.permutation(8)
