@@ -13,13 +13,15 @@ import os
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EALIGN, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EALIGN, ATTN_EWORKSPACE, ATTN_EHIP, \
+    ATTN_ESCRATCH = range(7)
+ATTN_DECODE_SCRATCH_BYTES = 16 << 20   # include/attn.h
 ATTN_FP32, ATTN_FP16, ATTN_BF16 = 0, 1, 2
 ATTN_BHND, ATTN_BNHD = 0, 1
 
 EXPORTS = ("attn_validate", "attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_decode_workspace_bytes", "attn_decode", "attn_quantize_fp8", "attn_fwd_fp8",
-           "attn_status_string")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_decode_static",
+           "attn_quantize_fp8", "attn_fwd_fp8", "attn_status_string")
 
 
 class AttnParams(ctypes.Structure):
@@ -70,6 +72,8 @@ def load():
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_static.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.attn_decode_static.restype = ctypes.c_int
     lib.attn_quantize_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_quantize_fp8.restype = ctypes.c_int
     lib.attn_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -277,6 +281,28 @@ def attn_decode(q, k, v, *, layout="bhnd", causal=False, scale=None, kv_lens=Non
                          _stream_ptr(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+    return out, lse
+
+
+def attn_decode_static(q, k, v, *, layout="bhnd", causal=False, scale=None, kv_lens=None,
+                       window_size=(-1, -1), softcap=0.0, out=None, lse=None):
+    """attn_decode with the library's fixed per-GPU scratch instead of a
+    workspace (no device allocation by the library; out / lse are allocated
+    here unless given).  Arguments and result as for attn_decode."""
+    torch = _torch()
+    lib = load()
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v, layout)
+    kv_lens, lens_ptr = _lens_arg(kv_lens, B)
+    p = make_params(B, Hq, Hkv, Nq, Nk, d, _dtype_code(q.dtype), _layout_code(layout), scale,
+                    causal, None, (0, 0, 0), lens_ptr, window_size, None, softcap)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_static(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), lse.data_ptr(), _stream_ptr(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_static")
     return out, lse
 
 

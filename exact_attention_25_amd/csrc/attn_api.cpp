@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "attn_kernels.h"
 
@@ -308,20 +310,26 @@ size_t attn_decode_workspace_bytes(const attn_params* p) {
   return t > 0 ? t : 256;
 }
 
-attn_status attn_decode(const attn_params* p, const void* q, const void* k, const void* v,
-                        void* o, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  const attn_status st = validate_decode(p);
-  if (st != ATTN_OK) return st;
-  if (p->B == 0 || p->Nq == 0) return ATTN_OK;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a decode call that need no workspace.
+attn_status check_decode_args(const attn_params* p, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse) {
   if (!q || !o || !lse) return ATTN_EINVAL;
   if (p->Nk > 0 && (!k || !v)) return ATTN_EINVAL;
-  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  const void* ptrs[] = {q, k, v, o, lse};
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return ATTN_EALIGN;
   if (p->kv_lens && (reinterpret_cast<uintptr_t>(p->kv_lens) & 3u)) return ATTN_EALIGN;
-  if (!workspace || workspace_bytes < attn_decode_workspace_bytes(p)) return ATTN_EWORKSPACE;
+  return ATTN_OK;
+}
 
+// The decode launch on a checked call with a workspace of at least
+// decode_workspace(p).total bytes.
+attn_status run_decode(const attn_params* p, const void* q, const void* k, const void* v,
+                       void* o, float* lse, void* workspace, void* stream) {
   const DecodeWorkspace ws = decode_workspace(p);
   attn::DecodeArgs a = {};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -352,6 +360,63 @@ attn_status attn_decode(const attn_params* p, const void* q, const void* k, cons
   const hipError_t e = attn::launch_decode(a, p->dtype == ATTN_BF16, p->softcap > 0.0f,
                                            reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+// Scratch of attn_decode_static: one copy per GPU, for callers that cannot
+// allocate.  Host code never uses this name as an address: it takes the
+// device address of the current GPU's copy from hipGetSymbolAddress, once
+// per device (scratch_ptr below).
+static __device__ __align__(256) char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current GPU's scratch (nullptr on failure).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode(const attn_params* p, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const attn_status st = validate_decode(p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Nq == 0) return ATTN_OK;
+  const attn_status ca = check_decode_args(p, q, k, v, o, lse);
+  if (ca != ATTN_OK) return ca;
+  if (workspace && !aligned16(workspace)) return ATTN_EALIGN;
+  if (!workspace || workspace_bytes < attn_decode_workspace_bytes(p)) return ATTN_EWORKSPACE;
+  return run_decode(p, q, k, v, o, lse, workspace, stream);
+}
+
+attn_status attn_decode_static(const attn_params* p, const void* q, const void* k,
+                               const void* v, void* o, float* lse, void* stream) {
+  const attn_status st = validate_decode(p);
+  if (st != ATTN_OK) return st;
+  if (p->B == 0 || p->Nq == 0) return ATTN_OK;
+  const attn_status ca = check_decode_args(p, q, k, v, o, lse);
+  if (ca != ATTN_OK) return ca;
+  if (decode_workspace(p).total > (size_t)ATTN_DECODE_SCRATCH_BYTES) return ATTN_ESCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return ATTN_EHIP;
+  return run_decode(p, q, k, v, o, lse, ws, stream);
 }
 
 }  // extern "C"
@@ -453,7 +518,8 @@ const char* attn_status_string(attn_status s) {
     case ATTN_EINVAL: return "invalid shape or parameter";
     case ATTN_EUNSUPPORTED: return "unsupported configuration";
     case ATTN_EALIGN: return "pointer not 16-byte aligned";
-    case ATTN_EWORKSPACE: return "backward workspace missing or too small";
+    case ATTN_EWORKSPACE: return "workspace missing or too small";
+    case ATTN_ESCRATCH: return "call needs more scratch than attn_decode_static's fixed buffer holds";
     case ATTN_EHIP: return "kernel launch failed";
   }
   return "unknown status";

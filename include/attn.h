@@ -53,8 +53,10 @@ typedef enum {
   ATTN_EINVAL = 1,        /* invalid shape or parameter                         */
   ATTN_EUNSUPPORTED = 2,  /* valid, but outside what the kernels implement      */
   ATTN_EALIGN = 3,        /* a pointer is not 16-byte aligned                   */
-  ATTN_EWORKSPACE = 4,    /* backward workspace missing or too small            */
-  ATTN_EHIP = 5           /* a kernel launch failed (hipGetLastError)           */
+  ATTN_EWORKSPACE = 4,    /* workspace missing or too small                     */
+  ATTN_EHIP = 5,          /* a kernel launch failed (hipGetLastError)           */
+  ATTN_ESCRATCH = 6       /* attn_decode_static: the call needs more scratch
+                             than ATTN_DECODE_SCRATCH_BYTES                     */
 } attn_status;
 
 typedef enum { ATTN_FP32 = 0, ATTN_FP16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -198,6 +200,27 @@ size_t attn_decode_workspace_bytes(const attn_params* p);
 attn_status attn_decode(const attn_params* p, const void* q, const void* k,
                         const void* v, void* o, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device scratch of attn_decode_static: 16 MiB, one copy
+ * per GPU, held from the library's load until the process ends. */
+#define ATTN_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* attn_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The key splits'
+ * partial outputs go to a static device array of ATTN_DECODE_SCRATCH_BYTES
+ * instead; results are those of attn_decode, bit for bit.
+ *   Arguments, layouts and errors as for attn_decode (no workspace); the
+ *   stream must belong to the current device, whose copy of the scratch is
+ *   used.  Returns ATTN_ESCRATCH, before enqueueing anything, when
+ *   attn_decode_workspace_bytes(p) > ATTN_DECODE_SCRATCH_BYTES; ATTN_EHIP if
+ *   the scratch's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (nothing in it needs clearing): calls that may overlap on
+ * one GPU (different streams, different host threads) race and must be
+ * ordered by the caller. */
+attn_status attn_decode_static(const attn_params* p, const void* q, const void* k,
+                               const void* v, void* o, float* lse, void* stream);
 
 /* FP8 block quantisation for attn_fwd_fp8 (the FP8 variant of
  * "FlashAttention技术解析：优化Transformer注意力计算效率" (jsqmd.com/news/722897)

@@ -129,7 +129,7 @@ def test_bwd_workspace_and_errors():
 
 def test_status_strings():
     seen = set()
-    for s in range(6):
+    for s in range(7):
         t = bd.attn_status_string(s)
         assert t and t not in seen
         seen.add(t)
@@ -220,3 +220,22 @@ def test_fp8_validation_and_errors():
     assert fwd() == bd.ATTN_EINVAL                                # null pointers
     assert quant() == bd.ATTN_EINVAL
     assert fwd(B=0) == bd.ATTN_OK and quant(B=0) == bd.ATTN_OK
+
+
+def test_decode_static_rejects_calls_beyond_its_scratch():
+    """attn_decode_static checks like attn_decode and refuses, before any
+    launch, a call whose split partials exceed ATTN_DECODE_SCRATCH_BYTES."""
+    lib = bd.load()
+    ptrs = [16 * (i + 1) for i in range(5)]   # q, k, v, o, lse (never dereferenced)
+    big = bd.make_params(64, 64, 8, 16, 65536, 128, bd.ATTN_BF16)
+    assert bd.attn_decode_workspace_bytes(big) > bd.ATTN_DECODE_SCRATCH_BYTES
+    assert lib.attn_decode_static(ctypes.byref(big), *ptrs, None) == bd.ATTN_ESCRATCH
+    small = bd.make_params(8, 32, 8, 1, 32768, 128, bd.ATTN_BF16)
+    assert bd.attn_decode_workspace_bytes(small) <= bd.ATTN_DECODE_SCRATCH_BYTES
+    # the same argument checks as attn_decode
+    masked = bd.make_params(8, 32, 8, 1, 32768, 128, bd.ATTN_BF16, mask_ptr=64)
+    assert lib.attn_decode_static(ctypes.byref(masked), *ptrs, None) == bd.ATTN_EUNSUPPORTED
+    bad = bd.make_params(8, 32, 5, 1, 32768, 128, bd.ATTN_BF16)
+    assert lib.attn_decode_static(ctypes.byref(bad), *ptrs, None) == bd.ATTN_EINVAL
+    assert lib.attn_decode_static(ctypes.byref(big), 16, 32, 48, 64, 8, None) == bd.ATTN_EALIGN
+    assert bd.attn_status_string(bd.ATTN_ESCRATCH).startswith("call needs more scratch")
