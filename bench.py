@@ -239,9 +239,42 @@ def cpu_baseline(w, x, budget_s=15.0, backward=False, decode=False, fp8=False):
             "fp64 numpy oracle forward"
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{what} on the first {done} of {w.B * w.Hq} (batch, head) pairs of "
-                      f"{w.name}, {dt:.1f} s; TFLOP/s counted like the GPU value"}
+                      f"{w.name}, {dt:.1f} s; TFLOP/s counted like the GPU value",
+            "tiny_fp32_one_core": tiny_one_core()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def tiny_one_core(reps=20):
+    """The oracle forward on the whole tiny fp32 workload (B1 H2 N128 d64) on
+    one BLAS thread: seconds per call (median of reps) and TFLOP/s."""
+    from threadpoolctl import threadpool_limits
+    from exact_attention_25_amd import accounting as acc
+    from exact_attention_25_amd import inputs
+    from oracle import ref_fwd
+    w = inputs.WORKLOADS["tiny_fp32_b1_h2_n128_d64"]
+    x = inputs.make_inputs(w, with_do=False)
+    ts = []
+    with threadpool_limits(1):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            ref_fwd(x["q"], x["k"], x["v"])
+            ts.append(time.perf_counter() - t0)
+    t = sorted(ts)[len(ts) // 2]
+    return {"seconds": round(t, 6), "cores": 1,
+            "tflops": round(acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False) / t / 1e12, 6)}
 
 
 def run_extras(device, steps, warmup):
@@ -307,6 +340,9 @@ def main():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--rotate", action="store_true",
+                    help="forward: cycle through copies of the inputs totalling >= 768 MB, so that "
+                         "they come from HBM (for the memory-bound workloads)")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch size (counter runs whose per-dispatch "
                          "cycle counts must stay below 2^31); the JSON line then names the new B")
@@ -357,7 +393,27 @@ def main():
         del src, dst
 
     lkw = local_kw(w)
-    fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"], **lkw)
+    # outputs allocated once, outside the timed calls
+    o_buf = torch.empty_like(t["q"])
+    l_buf = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=device)
+    fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"],
+                              out=o_buf, lse=l_buf, **lkw)
+    n_sets = 0
+    if args.rotate and args.which == "fwd":
+        # inputs (and outputs) rotated through >= 768 MB, so that every call
+        # reads its inputs from HBM rather than from the 256 MB last-level cache
+        sets = rotating_sets(t, w, 768 << 20)
+        for u in sets:
+            u["o"] = torch.empty_like(u["q"])
+            u["lse"] = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=device)
+        n_sets = len(sets)
+        rot = [0]
+
+        def fwd():
+            u = sets[rot[0] % n_sets]
+            rot[0] += 1
+            return bd.attn_fwd(u["q"], u["k"], u["v"], causal=w.causal, kv_lens=u["kv_lens"],
+                               out=u["o"], lse=u["lse"], **lkw)
     dec = args.which == "decode"
     fp8 = args.which == "fp8"
     if fp8:
@@ -469,7 +525,8 @@ def main():
         "data": f"synthetic (seeded N(0,1) inputs, numpy PCG64, rounded to {w.dtype}"
                 + (", then block-quantised to E4M3 by attn_quantize_fp8)" if fp8 else ")"),
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "Hkv": w.Hkv, "N": w.Nq,
-                   "d": w.d, "causal": w.causal, "mask": None, "key_padding": w.lens is not None,
+                   "Nk": w.Nk, "d": w.d, "causal": w.causal, "mask": None,
+                   "key_padding": w.lens is not None, "rotated_input_sets": n_sets,
                    "pass": "fp8 forward" if fp8 else ("backward" if bwd else "forward"),
                    **local_config(w)},
         "pct_of_peak": round(tflops / peak * 100, 2),
@@ -481,6 +538,15 @@ def main():
                                 if bwd else ("attn::fwd_fp8_kernel (one launch per step)" if fp8
                                              else fwd_kernel_name(w) + " (one launch per step)"))},
     }
+    if not (bwd or fp8) and w.name in HBM_BOUND:
+        # memory-bound forward: the roofline is HBM bandwidth over the
+        # algorithmic bytes (Q, K, V read once, O and LSE written once)
+        by = acc.fwd_min_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.dtype, x["kv_lens"] is not None)
+        gbs = by / ms / 1e6
+        rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": acc.PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gbs / acc.PEAK_HBM_GBS, 4),
+                           "traffic": None, "bytes_per_call": by,
+                           "kernel": rec["roofline"]["kernel"]}
     if fp8:
         rec["quantize_ms"] = round(q_ms, 4)
     if args.extras:
