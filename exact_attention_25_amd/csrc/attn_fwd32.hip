@@ -79,18 +79,38 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // K/V tiles are read 16 bytes at a time into registers one tile ahead (the
+  // next tile's loads are in flight while the current one is computed), then
+  // written to LDS; rows past kv_lens are zero, whatever the tensors hold.
+  constexpr int NL = BC * D / 4 / (NW * 64);   // float4 per thread per tensor
+  f32x4 kr[NL], vr[NL];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = (threadIdx.x + i * NW * 64) * 4;
+      const int r = e / D, c = e % D;
+      const bool ok = c < a.d && j0 + r < kv_limit;
+      const int64_t grow = ok ? j0 + r : 0;
+      kr[i] = ok ? *(const f32x4*)(kp + grow * a.k_sn + c) : f32x4{};
+      vr[i] = ok ? *(const f32x4*)(vp + grow * a.v_sn + c) : f32x4{};
+    }
+  };
+  if (t_begin < t_end) load_tile(t_begin * BC);
   for (int j = t_begin; j < t_end; ++j) {
     const int j0 = j * BC;
     __syncthreads();
-    for (int idx = threadIdx.x; idx < BC * D; idx += NW * 64) {
-      const int r = idx / D, c = idx % D;
-      // rows past kv_lens are zero, whatever the tensors hold there
-      const int grow = min(j0 + r, a.Nk - 1);
-      const bool ok = c < a.d && j0 + r < kv_limit;
-      ks_[r * LD + c] = ok ? kp[grow * a.k_sn + c] : 0.f;
-      vs_[r * LD + c] = ok ? vp[grow * a.v_sn + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = (threadIdx.x + i * NW * 64) * 4;
+      const int r = e / D, c = e % D;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ks_[r * LD + c + u] = kr[i][u];
+        vs_[r * LD + c + u] = vr[i][u];
+      }
     }
     __syncthreads();
+    if (j + 1 < t_end) load_tile(j0 + BC);
     uint32_t bits = 0;   // LOCAL: bit i set iff key j0 + i is visible to this lane's row
     if constexpr (LOCAL) {
       if (j < w_lo || j >= w_hi) continue;

@@ -6,8 +6,9 @@
 // (jsqmd.com/news/722897) §2.2 with the single final normalisation of its
 // §4.1 -- and bit-identical results; only the order of issue differs.
 //
-// Each wave owns 32 query rows; 8 waves (two per SIMD) share K/V tiles of BC
-// keys that stream through LDS, filled by direct buffer->LDS loads.  K runs
+// Each wave owns 32 query rows; the NW waves of a work-group (8, two per
+// SIMD; or 4, with two work-groups per CU) share K/V tiles of BC keys that
+// stream through LDS, filled by direct buffer->LDS loads.  K runs
 // one tile ahead of V: iteration j computes S of tile j+1 while it finishes
 // tile j, so the matrix cores have independent work while the vector unit
 // evaluates the exponentials:
@@ -15,8 +16,9 @@
 //   phase 1 (NQ steps):  one QK^T MFMA of tile j+1 per step, interleaved with
 //                        part of tile j's exponentials (p = exp2(s*c - m),
 //                        row sum, conversion to the 16-bit P operand), and
-//                        at every other step one of this wave's loads of
-//                        V(j+1) / K(j+2) into the buffers iteration j-1 used;
+//                        at every other step (every step with 4 waves) one
+//                        of this wave's loads of V(j+1) / K(j+2) into the
+//                        buffers iteration j-1 used;
 //   phase 2 (NP steps):  one PV MFMA of tile j per step; the first half of
 //                        the steps finish the exponentials (each 16-key
 //                        chunk before its first PV), the second half reduce
@@ -44,10 +46,12 @@
 
 namespace attn {
 
-template <class E, int D, int BC, bool CAUSAL>
+template <class E, int D, int BC, bool CAUSAL, int NW = 8>
 struct FwdPipeKernel {
   static constexpr float TH = 8.0f;                 // rescale threshold, log2 units
-  static constexpr int NW = 8;                      // waves per work-group
+  // NW waves per work-group: 8 (one work-group per CU), or 4 for short key
+  // ranges, where two independent work-groups per CU overlap one's start
+  // (Q and first K tile loads) with the other's tiles
   static constexpr int ROWS = NW * 32;              // query rows per work-group
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   // LDS row pitches in 16-byte slots: one pad slot per K row (the 16 rows one
@@ -199,7 +203,8 @@ struct FwdPipeKernel {
         if (do_k && ins < K_INS) dma16_buf(rk, st.koff[x - V_IPW], kdst + ins * 1024);
       }
     };
-    static_assert(V_IPW + K_IPW <= (NQ + 1) / 2, "the loads fit in phase 1");
+    constexpr int LSTEP = (V_IPW + K_IPW) * 2 <= NQ + 1 ? 2 : 1;   // steps per load
+    static_assert(V_IPW + K_IPW <= (NQ + LSTEP - 1) / LSTEP, "the loads fit in phase 1");
     const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
     float lsum = 0.f;
     V2 pp[NPAIR];
@@ -236,10 +241,10 @@ struct FwdPipeKernel {
     // In phase 1 the older wave of each SIMD pair (waves 0..3) otherwise wins
     // the issue arbitration and the younger one finishes ~80 % later; raising
     // the younger wave's priority for phase 1 evens them out a little.
-    if (st.wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
+    if (NW == 8 && st.wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      if ((i & 1) == 0) load_one(i >> 1);
+      if (i % LSTEP == 0) load_one(i / LSTEP);
       if (i + PF < NQ) kf[i + PF] = lds_read16<V8>(kaddr(st, kn, i + PF));
       else vload(i + PF - NQ);
       sn[i % KB] = E::mfma(kf[i], st.qf[i / KB], sn[i % KB]);
@@ -247,7 +252,7 @@ struct FwdPipeKernel {
       for (int p = (i * P1) / NQ; p < ((i + 1) * P1) / NQ; ++p) pair(p);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (st.wave >= NW / 2) __builtin_amdgcn_s_setprio(0);
+    if (NW == 8 && st.wave >= NW / 2) __builtin_amdgcn_s_setprio(0);
     // phase 2
     float mx = -INFINITY;
 #pragma unroll
@@ -405,10 +410,10 @@ struct FwdPipeKernel {
   }
 };
 
-template <class E, int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <class E, int D, int BC, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pipe_kernel(FwdArgs a) {
-  using K = FwdPipeKernel<E, D, BC, CAUSAL>;
+  using K = FwdPipeKernel<E, D, BC, CAUSAL, NW>;
   __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
