@@ -75,6 +75,8 @@ def fwd_kernel_name(w) -> str:
     if is_local(w) or w.softcap:
         return (f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal and not is_local(w)).lower()},"
                 f"mask=false,local={str(is_local(w)).lower()},softcap={str(bool(w.softcap)).lower()}>")
+    if w.d <= 64 and w.Nk <= 224:
+        return f"attn::fwd_resident_kernel<{e},causal={str(w.causal).lower()}>"
     span = min(w.Nq, w.Nk) if w.causal else w.Nk
     if span >= 8 * 64:
         nw = 4 if span <= 16 * 64 else 8
@@ -126,6 +128,41 @@ def time_calls(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_graph(fn, steps, warmup, outs):
+    """Per-call time of `steps` calls captured in one HIP graph and replayed:
+    the calls then run back to back on the GPU, without the host's per-call
+    launch time between them (which exceeds the kernel time of the smallest
+    workloads).  outs: the output tensors the calls write; every replay's
+    outputs are checked against an eager run's, bit for bit."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(o, r) for o, r in zip(outs, ref)):
+            raise RuntimeError("graph replay differs from the eager calls")
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return ms
 
 
 def call_percentiles(fn, n, stream):
@@ -320,10 +357,17 @@ def run_extras(device, steps, warmup):
                 return bd.attn_fwd(u["q"], u["k"], u["v"], causal=w.causal, kv_lens=u["kv_lens"],
                                    out=u["o"], lse=u["lse"])
             rms, _ = time_calls(rfn, max(steps, 2 * len(sets)), len(sets), stream)
+            # the same calls replayed from one HIP graph: kernel time without
+            # the host's launch time between calls
+            gms = time_graph(rfn, 2 * len(sets), len(sets),
+                             [x for u in sets for x in (u["o"], u["lse"])])
             rec.update({"fwd_ms_rotated": round(rms, 4),
                         "fwd_min_bytes_gbs_rotated": round(by / rms / 1e6, 1),
                         "rotated_sets": len(sets),
-                        "fwd_pct_hbm_peak_rotated": round(by / rms / 1e6 / acc.PEAK_HBM_GBS * 100, 1)})
+                        "fwd_pct_hbm_peak_rotated": round(by / rms / 1e6 / acc.PEAK_HBM_GBS * 100, 1),
+                        "fwd_ms_rotated_graph": round(gms, 4),
+                        "fwd_pct_hbm_peak_rotated_graph":
+                            round(by / gms / 1e6 / acc.PEAK_HBM_GBS * 100, 1)})
             del sets
         if w.backward:
             o, lse = fn()
@@ -354,6 +398,9 @@ def main():
     ap.add_argument("--rotate", action="store_true",
                     help="forward: cycle through copies of the inputs totalling >= 768 MB, so that "
                          "they come from HBM (for the memory-bound workloads)")
+    ap.add_argument("--graph", action="store_true",
+                    help="forward: time the steps as one captured HIP graph (back-to-back kernels, "
+                         "no host launch time between calls; for the microsecond-scale workloads)")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch size (counter runs whose per-dispatch "
                          "cycle counts must stay below 2^31); the JSON line then names the new B")
@@ -407,6 +454,7 @@ def main():
     # outputs allocated once, outside the timed calls
     o_buf = torch.empty_like(t["q"])
     l_buf = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=device)
+    outs = [o_buf, l_buf]
     fwd = lambda: bd.attn_fwd(t["q"], t["k"], t["v"], causal=w.causal, kv_lens=t["kv_lens"],
                               out=o_buf, lse=l_buf, **lkw)
     n_sets = 0
@@ -419,6 +467,7 @@ def main():
             u["lse"] = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=device)
         n_sets = len(sets)
         rot = [0]
+        outs = [x for u in sets for x in (u["o"], u["lse"])]
 
         def fwd():
             u = sets[rot[0] % n_sets]
@@ -463,7 +512,12 @@ def main():
         fn = fwd
         flops = fwd_flops_of(w, x["kv_lens"])
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
-    ms, wall = time_calls(fn, args.steps, args.warmup, stream)
+    graph = args.graph and args.which == "fwd"
+    if graph:
+        steps = args.steps if n_sets == 0 else -(-args.steps // n_sets) * n_sets
+        ms = time_graph(fn, steps, max(args.warmup, n_sets), outs)
+    else:
+        ms, _ = time_calls(fn, args.steps, args.warmup, stream)
 
     pct = call_percentiles(fn, min(args.steps, 50), stream)
 
@@ -538,6 +592,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "Hkv": w.Hkv, "N": w.Nq,
                    "Nk": w.Nk, "d": w.d, "causal": w.causal, "mask": None,
                    "key_padding": w.lens is not None, "rotated_input_sets": n_sets,
+                   "launch": "hip_graph" if graph else "eager",
                    "pass": "fp8 forward" if fp8 else ("backward" if bwd else "forward"),
                    **local_config(w)},
         "pct_of_peak": round(tflops / peak * 100, 2),

@@ -3,7 +3,8 @@
 // Nk) >= 8 tiles) take the software-pipelined kernel
 // (attn_fwd_pipe_kernel.h); the others take FwdKernel
 // (attn_fwd_kernel.h).  Both compute the same values.  Local and
-// soft-capped calls go to attn_fwd_local.hip.
+// soft-capped calls go to attn_fwd_local.hip; short key ranges at d <= 64
+// (Nk <= kResidentMaxKeys, no mask) to attn_fwd_resident.hip.
 #include "attn_fwd_kernel.h"
 #include "attn_fwd_pipe_kernel.h"
 
@@ -58,6 +59,8 @@ static hipError_t launch_fwd_e(const FwdArgs& a, bool causal, bool mask, hipStre
 
 hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st) {
   if (m.local || m.softcap) return launch_fwd16_local(a, is_bf16, m, st);
+  if (!m.mask && a.d <= 64 && a.Nk <= kResidentMaxKeys)
+    return launch_fwd16_resident(a, is_bf16, m.causal, st);
   return is_bf16 ? launch_fwd_e<BF16>(a, m.causal, m.mask, st)
                  : launch_fwd_e<FP16>(a, m.causal, m.mask, st);
 }

@@ -78,7 +78,6 @@ struct FwdKernel {
   // leave room for two work-groups per CU.  At d = 128 two.
   static constexpr int NST = D <= 64 ? 3 : 2;
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
-  static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "stages start on 1 KB boundaries");
   static constexpr int ROWS = NW * 32;              // query rows per block
   static constexpr int KB = BC / 32;                // 32-key blocks per tile
   static constexpr int KS = D / 16;                 // k-steps of QK^T
@@ -248,9 +247,14 @@ struct FwdKernel {
     }
     const float mref = st.m_run == -INFINITY ? 0.f : st.m_run;
     float lsum = 0.f;
+    // 16-key chunks wholly past kv_limit (the ragged end of the key range)
+    // hold only p = 0: their exponentials and PV products are skipped
+    const int live = __builtin_amdgcn_readfirstlane(st.kv_limit - j0);
     V8 pf[PT];
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
+      pf[t] = V8{};
+      if (t > 0 && t * 16 >= live) continue;
       const int k = t >> 1, r0 = (t & 1) * 8;
       typename E::V2 pp[4];
 #pragma unroll
@@ -270,6 +274,7 @@ struct FwdKernel {
     // O^T += V_j^T P^T
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
+      if (t > 0 && t * 16 >= live) continue;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const char* p = vbuf + st.vbase + t * 16 * VP + dt * 64;
@@ -331,10 +336,10 @@ struct FwdKernel {
   }
 
 
-  static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
-    auto kb = [&](int s) { return lds + s * STAGE_BYTES; };
-    auto vb = [&](int s) { return lds + s * STAGE_BYTES + K_BYTES; };
-    State st;
+  // Per-wave set-up: work-group -> (batch, head, query block), key range,
+  // load offsets, Q fragments, zero accumulators.  Returns the number of key
+  // tiles the block spans (before LOCAL narrows it).
+  static __device__ __forceinline__ int setup(const FwdArgs& a, State& st) {
     st.lane = threadIdx.x & 63;
     st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     st.hl = st.lane >> 5;
@@ -404,6 +409,16 @@ struct FwdKernel {
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
     st.m_run = -INFINITY;
     st.l_run = 0.f;
+    return n_tiles;
+  }
+
+  static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
+    static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "stages start on 1 KB boundaries");
+    auto kb = [&](int s) { return lds + s * STAGE_BYTES; };
+    auto vb = [&](int s) { return lds + s * STAGE_BYTES + K_BYTES; };
+    State st;
+    const int n_tiles = setup(a, st);
+    const int q_blk0 = st.q_w0 - st.wave * 32;
 
     // tiles [t_begin, t_end) pass through LDS
     int t_begin = 0, t_end = n_tiles;
@@ -438,8 +453,12 @@ struct FwdKernel {
       }
     }
 
-    // Epilogue.
-    T* op = (T*)a.o + b * a.o_sb + h * a.o_sh;
+    epilogue(a, st);
+  }
+
+  // O /= l (one reciprocal per row), rounded to the output type; LSE.
+  static __device__ __forceinline__ void epilogue(const FwdArgs& a, const State& st) {
+    T* op = (T*)a.o + st.b * a.o_sb + st.h * a.o_sh;
     const float l_tot = add_with_other_half(st.l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int row = st.q_w0 + st.l32;
@@ -458,7 +477,7 @@ struct FwdKernel {
         }
       }
       if (st.hl == 0)
-        a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] =
+        a.lse[((int64_t)st.b * a.Hq + st.h) * a.Nq + row] =
             l_tot > 0.f ? (st.m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
   }

@@ -1,0 +1,74 @@
+// Forward attention for short key ranges: every key tile of a (batch,
+// kv-head) resident in LDS at once.
+//
+// With a few key tiles per row (ViT-style sequences of a few hundred
+// tokens, cross-attention to a short context) the staged FwdKernel waits for
+// memory once per stage of tiles it streams, and the data of one work-group
+// is small, so each CU spends most of its time waiting with few bytes in
+// flight.  Here a work-group issues the loads of all its key tiles (32 keys
+// each, up to kResidentMaxKeys keys) together with its Q rows, waits once,
+// and then runs the tiles back to back without barriers; two work-groups
+// share a CU, so one's loads are in flight while the other computes.  The
+// per-tile arithmetic is FwdKernel's (the tiled online softmax of
+// "FlashAttention技术解析：优化Transformer注意力计算效率" (jsqmd.com/news/
+// 722897) §2.2, single final normalisation of §4.1), so the results are
+// those of FwdKernel with 32-key tiles.
+//
+// Taken by 16-bit calls with d <= 64, Nk <= kResidentMaxKeys and no
+// additive mask, window, neighbourhood or soft cap.
+#include "attn_fwd_kernel.h"
+
+namespace attn {
+
+template <class E, bool CAUSAL>
+struct FwdResidentKernel {
+  static constexpr int NW = 8, BC = 32, MAXT = kResidentMaxKeys / BC;
+  using F = FwdKernel<E, 64, NW, BC, CAUSAL, false>;
+  // a tile's K and V regions: whole 1 KB load instructions (the last one of
+  // each ends in pad slots that read as zero)
+  static constexpr int K_REGION = F::K_INS * 1024, V_REGION = F::V_INS * 1024;
+  static constexpr int TILE_BYTES = K_REGION + V_REGION;
+  static constexpr int LDS_BYTES = MAXT * TILE_BYTES;
+  static_assert(2 * LDS_BYTES <= 160 * 1024, "two work-groups per CU");
+
+  static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
+    typename F::State st;
+    const int n_tiles = F::setup(a, st);   // <= MAXT (Nk checked by the launch)
+    for (int j = 0; j < n_tiles; ++j)
+      F::issue(st, j * BC, lds + j * TILE_BYTES, lds + j * TILE_BYTES + K_REGION);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads (and Q) have landed
+    __syncthreads();                 // ... and every other wave's
+    st.ld_j0 = -1;                   // no loads inside the tiles
+    for (int j = 0; j < st.n_act; ++j)
+      F::tile(a, st, lds + j * TILE_BYTES, lds + j * TILE_BYTES + K_REGION, j * BC, 0);
+    F::epilogue(a, st);
+  }
+};
+
+// 512 threads, at most 128 VGPRs (four waves per SIMD): two work-groups per CU
+template <class E, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void fwd_resident_kernel(FwdArgs a) {
+  using K = FwdResidentKernel<E, CAUSAL>;
+  __shared__ __attribute__((aligned(1024))) char lds[K::LDS_BYTES];
+  K::run(a, lds);
+}
+
+template <class E>
+static hipError_t launch_t(const FwdArgs& a0, bool causal, hipStream_t st) {
+  FwdArgs a = a0;
+  a.nqb = (a.Nq + 255) / 256;
+  a.total_blocks = a.B * a.Hq * a.nqb;
+  if (causal)
+    hipLaunchKernelGGL((fwd_resident_kernel<E, true>), dim3(a.total_blocks), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_resident_kernel<E, false>), dim3(a.total_blocks), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd16_resident(const FwdArgs& a, bool is_bf16, bool causal, hipStream_t st) {
+  if (a.d > 64 || a.Nk > kResidentMaxKeys) return hipErrorInvalidValue;
+  return is_bf16 ? launch_t<BF16>(a, causal, st) : launch_t<FP16>(a, causal, st);
+}
+
+}  // namespace attn

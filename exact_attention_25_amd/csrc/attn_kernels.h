@@ -167,6 +167,10 @@ struct FwdMode {
 hipError_t launch_fwd16(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);
 // Local / soft-capped 16-bit launches (attn_fwd_local.hip).
 hipError_t launch_fwd16_local(const FwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);
+// Short key ranges with every key tile resident in LDS (attn_fwd_resident.hip):
+// 16-bit, d <= 64, Nk <= kResidentMaxKeys, no mask / window / cap.
+constexpr int kResidentMaxKeys = 224;
+hipError_t launch_fwd16_resident(const FwdArgs& a, bool is_bf16, bool causal, hipStream_t st);
 hipError_t launch_fwd32(const FwdArgs& a, FwdMode m, hipStream_t st);
 // Backward launches take the forward's mode (mode.mask: a.mask is set).
 hipError_t launch_bwd16(const BwdArgs& a, bool is_bf16, FwdMode m, hipStream_t st);

@@ -105,12 +105,15 @@ def test_forward_small(gpu_lib, case):
 # roles rotate with the tile index (loads run two tiles ahead): every key-tile
 # count from 1 to 7, so each count modulo 3 ends the loop at each stage, with
 # causal rows (per-wave tile counts), key lengths, an additive mask, GQA,
-# BNHD and ragged last tiles.  Nk < 512 keeps these on that kernel.
+# BNHD and ragged last tiles.  224 < Nk < 512 keeps these on that kernel
+# (shorter key ranges without a mask take the resident kernel below); the
+# one- to three-tile counts come from key lengths (drawn in 1..64, 65..128
+# and 129..192).
 STAGES = [
     # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, mask, layout
-    ("tiles1_d64", 2, 2, 1, 40, 50, 64, "bf16", False, None, None, "bhnd"),
-    ("tiles2_d64_fp16", 1, 2, 2, 70, 128, 64, "fp16", False, None, None, "bhnd"),
-    ("tiles3_d40", 2, 2, 2, 100, 150, 40, "bf16", False, None, None, "bhnd"),
+    ("tiles1_d64", 2, 2, 1, 40, 300, 64, "bf16", False, (20, 64), None, "bhnd"),
+    ("tiles2_d64_fp16", 1, 2, 2, 70, 260, 64, "fp16", False, (65, 128), None, "bhnd"),
+    ("tiles3_d40", 2, 2, 2, 100, 300, 40, "bf16", False, (129, 192), None, "bhnd"),
     ("tiles4_causal_d64", 1, 2, 1, 256, 256, 64, "bf16", True, None, None, "bhnd"),
     ("tiles4_5_lens_d64", 2, 2, 2, 130, 320, 64, "fp16", False, (200, 320), None, "bhnd"),
     ("tiles5_mask_d64", 1, 2, 2, 90, 300, 64, "bf16", False, None, "full11", "bhnd"),
@@ -130,6 +133,39 @@ def test_forward_stage_rotation(gpu_lib, case):
     o, lse = _run(w, x, layout=layout, causal=causal, mask=mask)
     O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], causal=causal, mask=mask,
                            kv_lens=x["kv_lens"])
+    check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
+
+
+# Short key ranges (Nk <= 224) at d <= 64 without a mask: every key tile of
+# the head resident in LDS (32-key tiles; 16-key chunks past the key range
+# skipped).  Key counts at the chunk and tile edges (16, 17, 32, 33, 48, 65,
+# 224), key lengths that end mid-chunk, causal (with key lengths), GQA, BNHD,
+# d = 8/32/40/64, query blocks past the first work-group, and 225 keys (the
+# first count the staged kernel takes) beside 224.
+RESIDENT = [
+    # id, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, layout
+    ("res_k16_d64", 1, 2, 2, 50, 16, 64, "bf16", False, None, "bhnd"),
+    ("res_k17_fp16", 2, 2, 1, 33, 17, 64, "fp16", False, None, "bhnd"),
+    ("res_k32_d32", 1, 3, 3, 64, 32, 32, "bf16", False, None, "bnhd"),
+    ("res_k33_lens", 2, 2, 2, 70, 33, 40, "fp16", False, (1, 33), "bhnd"),
+    ("res_k48_causal", 1, 2, 1, 48, 48, 64, "bf16", True, None, "bhnd"),
+    ("res_k65_causal", 1, 2, 2, 65, 65, 64, "fp16", True, None, "bhnd"),
+    ("res_k130_causal_gqa_lens", 2, 4, 2, 130, 130, 64, "bf16", True, (75, 130), "bhnd"),
+    ("res_k196_vit", 2, 3, 3, 196, 196, 64, "bf16", False, None, "bhnd"),
+    ("res_k224_rows600", 1, 2, 1, 600, 224, 40, "fp16", False, (150, 209), "bnhd"),
+    ("res_k224_d8", 1, 2, 2, 300, 224, 8, "bf16", False, None, "bhnd"),
+    ("staged_k225", 1, 2, 2, 300, 225, 64, "bf16", False, None, "bhnd"),
+]
+
+
+@pytest.mark.parametrize("case", RESIDENT, ids=[c[0] for c in RESIDENT])
+def test_forward_resident(gpu_lib, case):
+    name, B, Hq, Hkv, Nq, Nk, d, dtype, causal, lens, layout = case
+    _say(f"[fwd-resident] {name}")
+    w, x = make_case(B, Hq, Hkv, Nq, Nk, d, dtype, seed=zlib.crc32(name.encode()) % 10000,
+                     lens=lens)
+    o, lse = _run(w, x, layout=layout, causal=causal)
+    O_ref, L_ref = ref_fwd(x["q"], x["k"], x["v"], causal=causal, kv_lens=x["kv_lens"])
     check_out(from_layout(host(o), layout), lse, O_ref, L_ref, dtype, name)
 
 
