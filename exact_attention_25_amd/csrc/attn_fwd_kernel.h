@@ -77,7 +77,6 @@ struct FwdKernel {
   // tile ahead, so three stages (loads two tiles ahead) are kept; three still
   // leave room for two work-groups per CU.  At d = 128 two.
   static constexpr int NST = D <= 64 ? 3 : 2;
-  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int ROWS = NW * 32;              // query rows per block
   static constexpr int KB = BC / 32;                // 32-key blocks per tile
   static constexpr int KS = D / 16;                 // k-steps of QK^T
@@ -336,16 +335,15 @@ struct FwdKernel {
   }
 
 
-  // Per-wave set-up: work-group -> (batch, head, query block), key range,
+  // Per-wave set-up: block `wid` -> (batch, head, query block), key range,
   // load offsets, Q fragments, zero accumulators.  Returns the number of key
   // tiles the block spans (before LOCAL narrows it).
-  static __device__ __forceinline__ int setup(const FwdArgs& a, State& st) {
+  static __device__ __forceinline__ int setup(const FwdArgs& a, State& st, int wid) {
     st.lane = threadIdx.x & 63;
     st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     st.hl = st.lane >> 5;
     st.l32 = st.lane & 31;
 
-    const int wid = xcd_remap(blockIdx.x, a.total_blocks);
     int qblk = wid % a.nqb;
     const int bh = wid / a.nqb;
     const int h = bh % a.Hq;
@@ -412,12 +410,16 @@ struct FwdKernel {
     return n_tiles;
   }
 
-  static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
-    static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "stages start on 1 KB boundaries");
-    auto kb = [&](int s) { return lds + s * STAGE_BYTES; };
-    auto vb = [&](int s) { return lds + s * STAGE_BYTES + K_BYTES; };
+  // k[s] / v[s]: the K and V buffers of stage s, each its own LDS array, so
+  // that the compiler sees that a load into one stage does not write the
+  // stage being read (one array with offsets makes it wait for every
+  // outstanding load before each read of a tile)
+  static __device__ __forceinline__ void run(const FwdArgs& a, char* const (&k)[NST],
+                                             char* const (&v)[NST]) {
+    auto kb = [&](int s) { return k[s]; };
+    auto vb = [&](int s) { return v[s]; };
     State st;
-    const int n_tiles = setup(a, st);
+    const int n_tiles = setup(a, st, xcd_remap(blockIdx.x, a.total_blocks));
     const int q_blk0 = st.q_w0 - st.wave * 32;
 
     // tiles [t_begin, t_end) pass through LDS
@@ -462,20 +464,29 @@ struct FwdKernel {
     const float l_tot = add_with_other_half(st.l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int row = st.q_w0 + st.l32;
+    V8 seg[DT][2];   // 16-byte row segments (all lanes take part in the swaps)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        V4 g[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r = 8 * p + 4 * q;
+          const auto lo = E::cvt2(st.acc[dt][r + 0] * inv, st.acc[dt][r + 1] * inv);
+          const auto hi = E::cvt2(st.acc[dt][r + 2] * inv, st.acc[dt][r + 3] * inv);
+          g[q] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+        }
+        seg[dt][p] = out_segment16<V8, V4>(g[0], g[1]);
+      }
     if (row < a.Nq) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = dt * 32 + gq * 8 + st.hl * 4;
-          if (col < a.d) {
-            auto lo = E::cvt2(st.acc[dt][gq * 4 + 0] * inv, st.acc[dt][gq * 4 + 1] * inv);
-            auto hi = E::cvt2(st.acc[dt][gq * 4 + 2] * inv, st.acc[dt][gq * 4 + 3] * inv);
-            V4 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
-            *(V4*)(op + row * a.o_sn + col) = w;
-          }
+        for (int p = 0; p < 2; ++p) {
+          const int col = dt * 32 + (2 * p + st.hl) * 8;
+          if (col < a.d) *(V8*)(op + row * a.o_sn + col) = seg[dt][p];
         }
-      }
       if (st.hl == 0)
         a.lse[((int64_t)st.b * a.Hq + st.h) * a.Nq + row] =
             l_tot > 0.f ? (st.m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
@@ -488,8 +499,21 @@ template <class E, int D, int NW, int BC, bool CAUSAL, bool MASK, bool LOCAL = f
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void fwd_kernel(FwdArgs a) {
   using K = FwdKernel<E, D, NW, BC, CAUSAL, MASK, LOCAL, SOFTCAP>;
-  __shared__ __attribute__((aligned(1024))) char lds[K::NST * K::STAGE_BYTES];
-  K::run(a, lds);
+  __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[K::V_BYTES];
+  if constexpr (K::NST == 3) {
+    __shared__ __attribute__((aligned(1024))) char k2[K::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char v2[K::V_BYTES];
+    char* const kb[3] = {k0, k1, k2};
+    char* const vb[3] = {v0, v1, v2};
+    K::run(a, kb, vb);
+  } else {
+    char* const kb[2] = {k0, k1};
+    char* const vb[2] = {v0, v1};
+    K::run(a, kb, vb);
+  }
 }
 
 }  // namespace attn

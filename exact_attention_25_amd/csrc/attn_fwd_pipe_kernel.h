@@ -389,20 +389,29 @@ struct FwdPipeKernel {
     const float l_tot = add_with_other_half(st.l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int row = st.q_w0 + st.l32;
+    V8 seg[DT][2];   // 16-byte row segments (all lanes take part in the swaps)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        V4 g[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r = 8 * p + 4 * q;
+          const auto lo = E::cvt2(st.acc[dt][r + 0] * inv, st.acc[dt][r + 1] * inv);
+          const auto hi = E::cvt2(st.acc[dt][r + 2] * inv, st.acc[dt][r + 3] * inv);
+          g[q] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+        }
+        seg[dt][p] = out_segment16<V8, V4>(g[0], g[1]);
+      }
     if (row < a.Nq) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = dt * 32 + gq * 8 + st.hl * 4;
-          if (col < a.d) {
-            auto lo = E::cvt2(st.acc[dt][gq * 4 + 0] * inv, st.acc[dt][gq * 4 + 1] * inv);
-            auto hi = E::cvt2(st.acc[dt][gq * 4 + 2] * inv, st.acc[dt][gq * 4 + 3] * inv);
-            V4 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
-            *(V4*)(op + row * a.o_sn + col) = w;
-          }
+        for (int p = 0; p < 2; ++p) {
+          const int col = dt * 32 + (2 * p + st.hl) * 8;
+          if (col < a.d) *(V8*)(op + row * a.o_sn + col) = seg[dt][p];
         }
-      }
       if (st.hl == 0)
         a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] =
             l_tot > 0.f ? (st.m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;

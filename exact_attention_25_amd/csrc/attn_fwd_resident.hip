@@ -8,11 +8,15 @@
 // flight.  Here a work-group issues the loads of all its key tiles (32 keys
 // each, up to kResidentMaxKeys keys) together with its Q rows, waits once,
 // and then runs the tiles back to back without barriers; two work-groups
-// share a CU, so one's loads are in flight while the other computes.  The
-// per-tile arithmetic is FwdKernel's (the tiled online softmax of
-// "FlashAttention技术解析：优化Transformer注意力计算效率" (jsqmd.com/news/
-// 722897) §2.2, single final normalisation of §4.1), so the results are
-// those of FwdKernel with 32-key tiles.
+// share a CU.  The per-tile arithmetic is FwdKernel's (the tiled online
+// softmax of "FlashAttention技术解析：优化Transformer注意力计算效率"
+// (jsqmd.com/news/722897) §2.2, single final normalisation of §4.1), so the
+// results are those of FwdKernel with 32-key tiles.
+//
+// (A persistent form -- one work-group per CU walking the blocks with two
+// LDS buffers, the next block's loads under the current block's arithmetic
+// -- measured 25 % slower at ViT N = 196: the two buffers fill the CU's LDS,
+// which leaves two waves per SIMD instead of four.)
 //
 // Taken by 16-bit calls with d <= 64, Nk <= kResidentMaxKeys and no
 // additive mask, window, neighbourhood or soft cap.
@@ -24,23 +28,32 @@ template <class E, bool CAUSAL>
 struct FwdResidentKernel {
   static constexpr int NW = 8, BC = 32, MAXT = kResidentMaxKeys / BC;
   using F = FwdKernel<E, 64, NW, BC, CAUSAL, false>;
+  using State = typename F::State;
   // a tile's K and V regions: whole 1 KB load instructions (the last one of
   // each ends in pad slots that read as zero)
   static constexpr int K_REGION = F::K_INS * 1024, V_REGION = F::V_INS * 1024;
   static constexpr int TILE_BYTES = K_REGION + V_REGION;
-  static constexpr int LDS_BYTES = MAXT * TILE_BYTES;
-  static_assert(2 * LDS_BYTES <= 160 * 1024, "two work-groups per CU");
+  static constexpr int BUF_BYTES = MAXT * TILE_BYTES;    // every tile of one block
+  static_assert(2 * BUF_BYTES <= 160 * 1024, "two work-groups per CU");
 
-  static __device__ __forceinline__ void run(const FwdArgs& a, char* lds) {
-    typename F::State st;
-    const int n_tiles = F::setup(a, st);   // <= MAXT (Nk checked by the launch)
-    for (int j = 0; j < n_tiles; ++j)
-      F::issue(st, j * BC, lds + j * TILE_BYTES, lds + j * TILE_BYTES + K_REGION);
+  // this wave's loads of all n key tiles of the block set up in st
+  static __device__ __forceinline__ void issue_all(const State& st, int n, char* buf) {
+    for (int j = 0; j < n; ++j)
+      F::issue(st, j * BC, buf + j * TILE_BYTES, buf + j * TILE_BYTES + K_REGION);
+  }
+  static __device__ __forceinline__ void compute(const FwdArgs& a, State& st, const char* buf) {
+    st.ld_j0 = -1;   // no loads inside the tiles
+    for (int j = 0; j < st.n_act; ++j)
+      F::tile(a, st, buf + j * TILE_BYTES, buf + j * TILE_BYTES + K_REGION, j * BC, 0);
+  }
+
+  static __device__ __forceinline__ void run_one(const FwdArgs& a, char* buf) {
+    State st;
+    const int n = F::setup(a, st, xcd_remap(blockIdx.x, a.total_blocks));
+    issue_all(st, n, buf);           // n <= MAXT (Nk checked by the launch)
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads (and Q) have landed
     __syncthreads();                 // ... and every other wave's
-    st.ld_j0 = -1;                   // no loads inside the tiles
-    for (int j = 0; j < st.n_act; ++j)
-      F::tile(a, st, lds + j * TILE_BYTES, lds + j * TILE_BYTES + K_REGION, j * BC, 0);
+    compute(a, st, buf);
     F::epilogue(a, st);
   }
 };
@@ -50,8 +63,8 @@ template <class E, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_resident_kernel(FwdArgs a) {
   using K = FwdResidentKernel<E, CAUSAL>;
-  __shared__ __attribute__((aligned(1024))) char lds[K::LDS_BYTES];
-  K::run(a, lds);
+  __shared__ __attribute__((aligned(1024))) char lds[K::BUF_BYTES];
+  K::run_one(a, lds);
 }
 
 template <class E>
@@ -59,10 +72,11 @@ static hipError_t launch_t(const FwdArgs& a0, bool causal, hipStream_t st) {
   FwdArgs a = a0;
   a.nqb = (a.Nq + 255) / 256;
   a.total_blocks = a.B * a.Hq * a.nqb;
+  const dim3 grid(a.total_blocks);
   if (causal)
-    hipLaunchKernelGGL((fwd_resident_kernel<E, true>), dim3(a.total_blocks), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((fwd_resident_kernel<E, true>), grid, dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_resident_kernel<E, false>), dim3(a.total_blocks), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((fwd_resident_kernel<E, false>), grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

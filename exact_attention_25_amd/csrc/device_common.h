@@ -134,6 +134,26 @@ __device__ __forceinline__ float add_with_other_half(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Output rows of a 32x32 O^T accumulator in 16-byte segments.  Lane
+// (row r, half h) holds columns 8 g + 4 h .. 8 g + 4 h + 3 of row r in
+// registers 4 g .. 4 g + 3 (g = 0..3).  For a pair of groups (2p, 2p + 1),
+// converted to the 16-bit output type (lo: group 2p, hi: group 2p + 1), one
+// swap between lane r and lane r + 32 per dword leaves lane (r, h) with
+// columns 8 (2p + h) .. 8 (2p + h) + 7: one 16-byte store instead of two
+// 8-byte ones.  v_permlane32_swap exchanges the upper 32 lanes of its first
+// operand with the lower 32 lanes of its second.  All 64 lanes must take
+// part.
+template <class V8, class V4>
+__device__ __forceinline__ V8 out_segment16(V4 lo, V4 hi) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  const auto r0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+  const auto r1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+  const u32x4 w = {r0[0], r1[0], r0[1], r1[1]};
+  return __builtin_bit_cast(V8, w);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
