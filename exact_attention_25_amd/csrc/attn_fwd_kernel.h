@@ -59,14 +59,21 @@ struct FwdKernel {
   // is folded into the exponent)
   static constexpr bool PRE = MASK || SOFTCAP;
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  // LDS row pitches in 16-byte slots.  K rows get one pad slot: the 16 rows
-  // that one read instruction touches at a time (same chunk) then fall on 16
-  // different bank groups.  V rows get a pitch of 64 (mod 256) bytes: the
-  // transposed read takes 4 consecutive rows x 64 bytes per half-wave, which
-  // then cover all 64 banks.  Every read address is a per-lane base plus a
-  // compile-time offset.
-  static constexpr int KPS = CPR + 1;
-  static constexpr int VPS = CPR + 4;
+  // LDS row pitches in 16-byte slots.  At d = 128 K rows get one pad slot:
+  // the 16 rows that one read instruction touches at a time (same chunk) then
+  // fall on 16 different bank groups; V rows get a pitch of 64 (mod 256)
+  // bytes: the transposed read takes 4 consecutive rows x 64 bytes per
+  // half-wave, which then cover all 64 banks.  At d <= 64 (SWZ) rows are not
+  // padded -- a pad slot is a load lane that moves nothing, and short tiles
+  // are bound by load instructions -- and chunk c of row r sits at slot
+  // c ^ f(r) instead: f_K(r) = (r / 2) mod 8 spreads the 16 rows of a K read
+  // over the 16 bank groups, f_V(r) = 4 ((r / 2) mod 2) does the same for the
+  // 4 rows x 4 chunks of a half-wave's transposed V read.  Read addresses are
+  // per-lane bases plus compile-time offsets (one base per K k-step and per V
+  // d-tile under SWZ).
+  static constexpr bool SWZ = D == 64;
+  static constexpr int KPS = SWZ ? CPR : CPR + 1;
+  static constexpr int VPS = SWZ ? CPR : CPR + 4;
   static constexpr int KP = KPS * 16, VP = VPS * 16;   // pitches in bytes
   static constexpr int K_BYTES = BC * KP, V_BYTES = BC * VP;
   static constexpr int K_INS = (BC * KPS + 63) / 64;   // DMA instructions per K tile
@@ -107,6 +114,8 @@ struct FwdKernel {
     // chunk it copies, kBufOutOfRange for pad slots and columns past d
     uint32_t koff[K_IPW], voff[V_IPW];
     int kbase, vbase;           // per-lane LDS byte offsets of the read patterns
+    int kofs[SWZ ? KS : 1];     // SWZ: per k-step K read offsets
+    int vofs[SWZ ? DT : 1];     // SWZ: per d-tile V read offsets
     float c;                    // scale * log2(e)
     V8 qf[KS];                  // Q fragments (B operand of S^T = K Q^T)
     f32x16 acc[DT];             // O^T accumulators
@@ -114,11 +123,14 @@ struct FwdKernel {
   };
 
   // Byte offset, within a tile of row pitch sn elements, of the chunk that
-  // lane copies in DMA instruction `ins` of a tile with `ps` slots per row.
+  // lane copies in DMA instruction `ins` of a tile with `ps` slots per row
+  // (is_v: the V tile, whose swizzle differs under SWZ).
   static __device__ __forceinline__ uint32_t dma_offset(int ins, int lane, int ps, int dchunks,
-                                                        int64_t sn) {
+                                                        int64_t sn, bool is_v) {
     const int s = ins * 64 + lane;
-    const int r = s / ps, ch = s % ps;
+    const int r = s / ps;
+    int ch = s % ps;
+    if (SWZ) ch ^= is_v ? 4 * ((r >> 1) & 1) : (r >> 1) & 7;
     if (r >= BC || ch >= dchunks) return kBufOutOfRange;
     return (uint32_t)((r * sn + ch * 8) * 2);
   }
@@ -172,7 +184,8 @@ struct FwdKernel {
       if (ks * 2 < K_IPW + V_IPW) { load_one(ks * 2); load_one(ks * 2 + 1); }
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
-        const V8 kf = lds_read16<V8>(kbuf + st.kbase + k * 32 * KP + ks * 32);
+        const V8 kf = SWZ ? lds_read16<V8>(kbuf + st.kofs[SWZ ? ks : 0] + k * 32 * KP)
+                          : lds_read16<V8>(kbuf + st.kbase + k * 32 * KP + ks * 32);
         s[k] = E::mfma(kf, st.qf[ks], s[k]);
       }
     }
@@ -276,7 +289,8 @@ struct FwdKernel {
       if (t > 0 && t * 16 >= live) continue;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const char* p = vbuf + st.vbase + t * 16 * VP + dt * 64;
+        const char* p = SWZ ? vbuf + st.vofs[SWZ ? dt : 0] + t * 16 * VP
+                            : vbuf + st.vbase + t * 16 * VP + dt * 64;
         const V4 lo = lds_read_tr4<V4>(p);
         const V4 hi = lds_read_tr4<V4>(p + 8 * VP);
         st.acc[dt] = E::mfma(concat4<V8, V4>(lo, hi), pf[t], st.acc[dt]);
@@ -375,10 +389,10 @@ struct FwdKernel {
     st.v_end = max(((int64_t)(st.kv_limit - 1) * a.v_sn + a.d) * 2, (int64_t)0);
 #pragma unroll
     for (int i = 0; i < K_IPW; ++i)
-      st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn);
+      st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn, false);
 #pragma unroll
     for (int i = 0; i < V_IPW; ++i)
-      st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn);
+      st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn, true);
     st.dma_n = 0;
 #pragma unroll
     for (int i = 0; i < K_IPW; ++i) st.dma_n += i * NW + st.wave < K_INS;
@@ -392,6 +406,21 @@ struct FwdKernel {
     {
       const int grp = st.lane >> 4, gi = st.lane & 15;
       st.vbase = (4 * (grp >> 1) + (gi >> 2)) * VP + (16 * (grp & 1) + 4 * (gi & 3)) * 2;
+      if constexpr (SWZ) {
+        // K: chunk 2 ks + hl of row l32 (+32 k: same f_K); V: chunk
+        // 2 (group % 2) + (i % 4) / 2 + 4 dt of row 4 (group / 2) + i / 4
+        // (+16 t, +8: same f_V), byte 8 (i % 2) within it
+        const int fk = (st.l32 >> 1) & 7;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          st.kofs[SWZ ? ks : 0] = st.l32 * KP + (((2 * ks + st.hl) ^ fk) * 16);
+        const int vr = 4 * (grp >> 1) + (gi >> 2);
+        const int vc = 2 * (grp & 1) + ((gi & 3) >> 1);
+        const int fv = 4 * ((vr >> 1) & 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          st.vofs[SWZ ? dt : 0] = vr * VP + (((vc + 4 * dt) ^ fv) * 16) + (gi & 1) * 8;
+      }
     }
 
     const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh;
