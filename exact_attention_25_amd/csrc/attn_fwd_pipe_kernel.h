@@ -54,11 +54,18 @@ struct FwdPipeKernel {
   // (Q and first K tile loads) with the other's tiles
   static constexpr int ROWS = NW * 32;              // query rows per work-group
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  // LDS row pitches in 16-byte slots: one pad slot per K row (the 16 rows one
-  // K read touches at a time fall on distinct banks), four per V row (the
-  // transposed read takes 4 rows x 64 bytes per half-wave).
-  static constexpr int KPS = CPR + 1;
-  static constexpr int VPS = CPR + 4;
+  // LDS rows of CPR 16-byte slots, unpadded (a pad slot would be a load lane
+  // that moves nothing); chunk c of row r sits at slot c ^ f(r), which puts
+  // the 16 rows one K read touches at a time (same chunk) on 16 different
+  // bank groups, and likewise the 4 rows x 4 chunks of a half-wave's
+  // transposed V read: at d = 128 (256-byte rows) f_K(r) = r mod 16 and
+  // f_V(r) = 4 (r mod 4); at d = 64 (two rows per 256 bytes)
+  // f_K(r) = (r / 2) mod 8 and f_V(r) = 4 ((r / 2) mod 2).  The loads pick
+  // their source chunk accordingly; the read bases fold the XOR in.
+  static constexpr int KPS = CPR;
+  static constexpr int VPS = CPR;
+  static __host__ __device__ constexpr int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __host__ __device__ constexpr int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
   static constexpr int KP = KPS * 16, VP = VPS * 16;
   static constexpr int K_BYTES = BC * KP, V_BYTES = BC * VP;
   static constexpr int K_INS = (BC * KPS + 63) / 64;   // load instructions per K tile
@@ -93,7 +100,7 @@ struct FwdPipeKernel {
     int64_t k_tile, v_tile;     // bytes between consecutive tiles
     int64_t k_end, v_end;       // bytes from kp / vp to the end of key kv_limit-1
     uint32_t koff[K_IPW], voff[V_IPW];  // per load instruction: byte offset in a tile
-    int kbase, vbase;           // per-lane LDS byte offsets of the read patterns
+    int kofs[KS], vofs[DT];     // per-lane LDS byte offsets: K per k-step, V per d-tile
     float c;                    // scale * log2(e)
     V8 qf[KS];                  // Q fragments (B operand of S^T = K Q^T)
     f32x16 acc[DT];             // O^T accumulators
@@ -105,9 +112,10 @@ struct FwdPipeKernel {
   // LDS slots per row; pad slots and columns past d get an out-of-range
   // offset (the load returns zero).
   static __device__ __forceinline__ uint32_t dma_offset(int ins, int lane, int ps, int dchunks,
-                                                        int64_t sn) {
+                                                        int64_t sn, bool is_v) {
     const int s = ins * 64 + lane;
-    const int r = s / ps, ch = s % ps;
+    const int r = s / ps;
+    const int ch = (s % ps) ^ (is_v ? fv(r) : fk(r));
     if (r >= BC || ch >= dchunks) return kBufOutOfRange;
     return (uint32_t)((r * sn + ch * 8) * 2);
   }
@@ -132,7 +140,7 @@ struct FwdPipeKernel {
   }
 
   static __device__ __forceinline__ const char* kaddr(const State& st, const char* kbuf, int i) {
-    return kbuf + st.kbase + (i % KB) * 32 * KP + (i / KB) * 32;
+    return kbuf + st.kofs[i / KB] + (i % KB) * 32 * KP;
   }
 
   static __device__ __forceinline__ void qk_plain(const State& st, const char* kbuf, Scores& s) {
@@ -211,7 +219,7 @@ struct FwdPipeKernel {
     V8 kf[NQ];
     V8 vf[NP];
     auto vload = [&](int i) {
-      const char* p = vc + st.vbase + (i / DT) * 16 * VP + (i % DT) * 64;
+      const char* p = vc + st.vofs[i % DT] + (i / DT) * 16 * VP;
       const V4 lo = lds_read_tr4<V4>(p);
       const V4 hi = lds_read_tr4<V4>(p + 8 * VP);
       vf[i] = concat4<V8, V4>(lo, hi);
@@ -333,18 +341,23 @@ struct FwdPipeKernel {
     st.v_end = max(((int64_t)(st.kv_limit - 1) * a.v_sn + a.d) * 2, (int64_t)0);
 #pragma unroll
     for (int i = 0; i < K_IPW; ++i)
-      st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn);
+      st.koff[i] = dma_offset(i * NW + st.wave, st.lane, KPS, dchunks, a.k_sn, false);
 #pragma unroll
     for (int i = 0; i < V_IPW; ++i)
-      st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn);
+      st.voff[i] = dma_offset(i * NW + st.wave, st.lane, VPS, dchunks, a.v_sn, true);
     // K read: lane holds key row l32 (+32 k), chunk 2 ks + hl.
-    st.kbase = st.l32 * KP + st.hl * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      st.kofs[ks] = st.l32 * KP + (((2 * ks + st.hl) ^ fk(st.l32)) * 16);
     // V transposed read: in each 16-lane group lane i points at row
     // 4 (group / 2) + i / 4 (+16 t, +8), column 16 (group % 2) + 4 (i % 4)
     // (+32 dt), so that lane l gets column l of four consecutive rows.
     {
       const int grp = st.lane >> 4, gi = st.lane & 15;
-      st.vbase = (4 * (grp >> 1) + (gi >> 2)) * VP + (16 * (grp & 1) + 4 * (gi & 3)) * 2;
+      const int vr = 4 * (grp >> 1) + (gi >> 2), vcol = 2 * (grp & 1) + ((gi & 3) >> 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        st.vofs[dt] = vr * VP + (((vcol + 4 * dt) ^ fv(vr)) * 16) + (gi & 1) * 8;
     }
 
     const T* qp = (const T*)a.q + b * a.q_sb + h * a.q_sh;
