@@ -80,7 +80,8 @@ def fwd_kernel_name(w) -> str:
     span = min(w.Nq, w.Nk) if w.causal else w.Nk
     if span >= 8 * 64:
         nw = 4 if span <= 16 * 64 else 8
-        return f"attn::fwd_pipe_kernel<{e},{D},64,causal={str(w.causal).lower()},NW={nw}>"
+        bc = 128 if (D == 64 and nw == 8) else 64
+        return f"attn::fwd_pipe_kernel<{e},{D},{bc},causal={str(w.causal).lower()},NW={nw}>"
     return f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal).lower()},mask=false>"
 
 

@@ -34,7 +34,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a0, bool causal, bool mask, hipStr
     // up to 16 key tiles: 4-wave work-groups, two per CU (measured +3.5 % at
     // 1024 keys, -3 % at 4096)
     if (span <= 16 * BC) return launch_pipe<E, D, BC, 4>(a0, causal, st);
-    return launch_pipe<E, D, BC, 8>(a0, causal, st);
+    // d <= 64: 128-key tiles, which halve the per-tile work outside the
+    // products (row-maximum exchange, rescale test, barrier) per key; the
+    // scores of two such tiles still fit in the registers (measured +10 % at
+    // N = 4096, d = 40)
+    if constexpr (D == 64) return launch_pipe<E, D, 2 * BC, 8>(a0, causal, st);
+    else return launch_pipe<E, D, BC, 8>(a0, causal, st);
   }
   using K = FwdKernel<E, D, NW, BC, false, false>;
   FwdArgs a = a0;

@@ -65,6 +65,10 @@ SMALL = [
     ("bf16_d40_pipe_bnhd_tail", 1, 3, 3, 70, 515, 40, "bf16", False, None, None, "bnhd", None, 1.0),
     ("fp16_d128_pipe_large_logits", 1, 2, 2, 64, 1030, 128, "fp16", False, None, None, "bhnd", 2.0, 1.0),
     ("bf16_d128_pipe_one_tile", 2, 1, 1, 40, 520, 128, "bf16", False, (3, 64), None, "bhnd", None, 1.0),
+    # d <= 64 beyond 1024 keys: the pipelined kernel with 128-key tiles
+    ("fp16_d64_pipe128_causal_lens", 2, 2, 1, 1300, 1300, 64, "fp16", True, (700, 1300), None, "bhnd", None, 1.0),
+    ("bf16_d40_pipe128_bnhd_ragged", 1, 3, 3, 150, 1500, 40, "bf16", False, None, None, "bnhd", None, 1.0),
+    ("fp16_d64_pipe128_large_logits", 1, 2, 2, 64, 1100, 64, "fp16", False, (1030, 1100), None, "bhnd", None, 3.0),
 ]
 
 
