@@ -66,6 +66,21 @@
 namespace attn {
 
 
+// Register placement.  These kernels need more than the 256 VGPRs of a
+// wave, so part of their state lives in AGPRs, which only the matrix cores
+// read and write directly.  The fragments a kernel keeps for its whole
+// life (K and V in the dK/dV kernel, Q and dO in the dQ kernel) are only
+// ever MFMA A/B operands, which may come from AGPRs; pin_agpr places them
+// there.  The sources are compiled with the MFMA results in VGPRs
+// (-amdgpu-mfma-vgpr-form, set by build.py), so S, dP and the gradient
+// accumulators, which the vector code reads, stay in VGPRs and no
+// AGPR->VGPR copy is issued per element.
+template <class V, int N>
+__device__ __forceinline__ void pin_agpr(V (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]));
+}
+
 // 8 x 16-bit input values -> 8 x fp16 (identity for fp16 inputs).
 template <class E>
 __device__ __forceinline__ f16x8 to_f16x8(typename E::V8 x) {
@@ -559,6 +574,8 @@ struct BwdQ {
         st.qf[ks] = d0 < a.d ? to_f16x8_scaled<E>(*(const V8*)(qp + d0), sc.q) : H8{};
         st.df[ks] = d0 < a.d ? scale_v8<E>(*(const V8*)(dp + d0), sc.dout * sc.v) : V8{};
       }
+      pin_agpr(st.qf);
+      pin_agpr(st.df);
     }
     const float lse = a.lse[((int64_t)b * a.Hq + h) * a.Nq + crow];
     st.nl2 = (st.qrow < a.Nq && lse != -INFINITY) ? -lse * kLog2e : -INFINITY;
@@ -979,6 +996,8 @@ struct BwdKV {
         st.kf[ks] = d0 < a.d ? to_f16x8_scaled<E>(*(const V8*)(kp + d0), sc.k) : H8{};
         st.vf[ks] = d0 < a.d ? to_f16x8_scaled<E>(*(const V8*)(vp + d0), sc.v) : H8{};
       }
+      pin_agpr(st.kf);
+      pin_agpr(st.vf);
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
