@@ -166,6 +166,56 @@ def time_graph(fn, steps, warmup, outs):
     return ms
 
 
+def sample_sclk(fn, ms_per_call, max_s=10.0):
+    """Mean engine clock (MHz) over the XCDs while fn() runs back to back.
+
+    amd-smi is read once from a second thread, half a second into a stretch
+    of calls; the calls go in batches of ~20 ms with a synchronisation after
+    each, so the GPU stays loaded until the reading is taken and the queue
+    never runs far ahead.  None if amd-smi is missing or prints no clock."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    exe = "/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else shutil.which("amd-smi")
+    if not exe:
+        return None
+    got = {}
+
+    def probe():
+        time.sleep(0.5)
+        try:
+            r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True, text=True,
+                               timeout=20)
+            d = json.loads(r.stdout)
+            clocks = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
+            vals = [float(v["clk"]["value"]) for k, v in clocks.items()
+                    if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+            got["mhz"] = sum(vals) / len(vals) if vals else None
+        except Exception:
+            got["mhz"] = None
+
+    batch = max(1, int(20.0 / max(ms_per_call, 1e-3)))
+    th = threading.Thread(target=probe, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < max_s:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    return got.get("mhz")
+
+
+def clock_fields(mhz, value, peak) -> dict:
+    """The engine clock under load and the %-of-peak at that clock (the
+    published peaks assume 2400 MHz)."""
+    if not mhz:
+        return {"sclk_mhz_under_load": None}
+    return {"sclk_mhz_under_load": round(mhz),
+            "pct_of_peak_at_measured_clock": round(value / (peak * mhz / 2400.0) * 100, 2)}
+
+
 def call_percentiles(fn, n, stream):
     """Per-call durations (ms) of n further calls, each bracketed by its own
     HIP events on the launch stream: p10, p50, p90."""
@@ -396,6 +446,8 @@ def main():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the engine-clock reading (amd-smi, ~1 s of extra calls)")
     ap.add_argument("--rotate", action="store_true",
                     help="forward: cycle through copies of the inputs totalling >= 768 MB, so that "
                          "they come from HBM (for the memory-bound workloads)")
@@ -521,6 +573,7 @@ def main():
         ms, _ = time_calls(fn, args.steps, args.warmup, stream)
 
     pct = call_percentiles(fn, min(args.steps, 50), stream)
+    mhz = None if args.no_clock else sample_sclk(fn, ms)
 
     tflops = flops / ms / 1e9
     peak = acc.PEAK_TFLOPS["fp8" if fp8 else w.dtype]
@@ -545,6 +598,7 @@ def main():
                        "key_padding": w.lens is not None, "pass": "decode",
                        **local_config(w)},
             "pct_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS * 100, 2),
+            "sclk_mhz_under_load": round(mhz) if mhz else None,
             "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": acc.PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / acc.PEAK_HBM_GBS, 4),
@@ -597,6 +651,7 @@ def main():
                    "pass": "fp8 forward" if fp8 else ("backward" if bwd else "forward"),
                    **local_config(w)},
         "pct_of_peak": round(tflops / peak * 100, 2),
+        **clock_fields(mhz, tflops, peak),
         "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
