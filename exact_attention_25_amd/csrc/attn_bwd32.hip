@@ -61,11 +61,9 @@ __global__ __launch_bounds__(256) void bwd32_q_kernel(BwdArgs a) {
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int nqb = (a.Nq + ROWS - 1) / ROWS;
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
-  int qblk = wid % nqb;
-  const int bh = wid / nqb;
+  int qblk, bh;
+  block_coords(CAUSAL, blockIdx.x, a.B * a.Hq, nqb, qblk, bh);
   const int h = bh % a.Hq, b = bh / a.Hq;
-  if (CAUSAL) qblk = nqb - 1 - qblk;
   const int g = h / a.group;
   const int q_blk0 = qblk * ROWS;
   const int q_w0 = q_blk0 + wave * 32;

@@ -546,11 +546,9 @@ struct BwdQ {
     st.l32 = st.lane & 31;
 
     const int nqb = (a.Nq + ROWS - 1) / ROWS;
-    const int wid = xcd_remap(blockIdx.x, gridDim.x);
-    int qblk = wid % nqb;
-    const int bh = wid / nqb;
+    int qblk, bh;
+    block_coords(CAUSAL, blockIdx.x, a.B * a.Hq, nqb, qblk, bh);
     const int h = bh % a.Hq, b = bh / a.Hq;
-    if (CAUSAL) qblk = nqb - 1 - qblk;
     const int g = h / a.group;
     const int q_blk0 = qblk * ROWS;
     st.q_w0 = q_blk0 + st.wave * 32;

@@ -326,11 +326,9 @@ struct Fp8Fwd {
     st.hl = st.lane >> 5;
     st.l32 = st.lane & 31;
 
-    const int wid = xcd_remap(blockIdx.x, a.total_blocks);
-    int qblk = wid % a.nqb;
-    const int bh = wid / a.nqb;
+    int qblk, bh;
+    block_coords(CAUSAL, blockIdx.x, a.B * a.Hq, a.nqb, qblk, bh);
     const int h = bh % a.Hq, b = bh / a.Hq;
-    if (CAUSAL) qblk = a.nqb - 1 - qblk;   // longest rows first
     const int g = h / a.group;
     st.b = b;
     st.h = h;

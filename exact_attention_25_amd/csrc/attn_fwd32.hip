@@ -30,11 +30,9 @@ __global__ __launch_bounds__(256) void fwd32_kernel(FwdArgs a) {
   const int wave = threadIdx.x >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
 
-  const int wid = xcd_remap(blockIdx.x, a.total_blocks);
-  int qblk = wid % a.nqb;
-  const int bh = wid / a.nqb;
+  int qblk, bh;
+  block_coords(CAUSAL, blockIdx.x, a.B * a.Hq, a.nqb, qblk, bh);
   const int h = bh % a.Hq, b = bh / a.Hq;
-  if (CAUSAL) qblk = a.nqb - 1 - qblk;
   const int g = h / a.group;
   const int q_blk0 = qblk * ROWS;
   const int q_w0 = q_blk0 + wave * 32;

@@ -352,19 +352,18 @@ struct FwdKernel {
   // Per-wave set-up: block `wid` -> (batch, head, query block), key range,
   // load offsets, Q fragments, zero accumulators.  Returns the number of key
   // tiles the block spans (before LOCAL narrows it).
-  static __device__ __forceinline__ int setup(const FwdArgs& a, State& st, int wid) {
+  static __device__ __forceinline__ int setup(const FwdArgs& a, State& st, int hw_id) {
     st.lane = threadIdx.x & 63;
     st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     st.hl = st.lane >> 5;
     st.l32 = st.lane & 31;
 
-    int qblk = wid % a.nqb;
-    const int bh = wid / a.nqb;
+    int qblk, bh;
+    block_coords(CAUSAL, hw_id, a.B * a.Hq, a.nqb, qblk, bh);
     const int h = bh % a.Hq;
     const int b = bh / a.Hq;
     st.b = b;
     st.h = h;
-    if (CAUSAL) qblk = a.nqb - 1 - qblk;  // longest rows first
     const int g = h / a.group;
     const int q_blk0 = qblk * ROWS;
     st.q_w0 = q_blk0 + st.wave * 32;
@@ -448,7 +447,7 @@ struct FwdKernel {
     auto kb = [&](int s) { return k[s]; };
     auto vb = [&](int s) { return v[s]; };
     State st;
-    const int n_tiles = setup(a, st, xcd_remap(blockIdx.x, a.total_blocks));
+    const int n_tiles = setup(a, st, blockIdx.x);
     const int q_blk0 = st.q_w0 - st.wave * 32;
 
     // tiles [t_begin, t_end) pass through LDS

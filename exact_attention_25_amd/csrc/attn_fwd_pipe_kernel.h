@@ -313,10 +313,8 @@ struct FwdPipeKernel {
     st.hl = st.lane >> 5;
     st.l32 = st.lane & 31;
 
-    const int wid = xcd_remap(blockIdx.x, a.total_blocks);
-    int qblk = wid % a.nqb;
-    if (CAUSAL) qblk = a.nqb - 1 - qblk;  // longest rows first
-    const int bh = wid / a.nqb;
+    int qblk, bh;
+    block_coords(CAUSAL, blockIdx.x, a.B * a.Hq, a.nqb, qblk, bh);
     const int h = bh % a.Hq;
     const int b = bh / a.Hq;
     const int g = h / a.group;

@@ -49,7 +49,7 @@ struct FwdResidentKernel {
 
   static __device__ __forceinline__ void run_one(const FwdArgs& a, char* buf) {
     State st;
-    const int n = F::setup(a, st, xcd_remap(blockIdx.x, a.total_blocks));
+    const int n = F::setup(a, st, blockIdx.x);
     issue_all(st, n, buf);           // n <= MAXT (Nk checked by the launch)
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads (and Q) have landed
     __syncthreads();                 // ... and every other wave's

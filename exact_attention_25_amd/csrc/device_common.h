@@ -166,6 +166,25 @@ __device__ __forceinline__ int xcd_remap(int hw_id, int total) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Work-group -> (query block, batch * head) for a grid of n_bh * nqb
+// work-groups.  Causal calls: the query block is the major index, last
+// (longest rows) first over the whole grid, so the long blocks of every
+// head start early and the short ones fill the end; each XCD (every 8th
+// work-group) then holds heads of every batch, whose key lengths may
+// differ, rather than whole batches.  Other calls: the query blocks of one
+// head run on one XCD (xcd_remap) and share its L2.
+__device__ __forceinline__ void block_coords(bool causal, int hw_id, int n_bh, int nqb, int& qblk,
+                                             int& bh) {
+  if (causal) {
+    qblk = nqb - 1 - hw_id / n_bh;
+    bh = hw_id % n_bh;
+  } else {
+    const int wid = xcd_remap(hw_id, n_bh * nqb);
+    qblk = wid % nqb;
+    bh = wid / nqb;
+  }
+}
+
 // Work-group id -> (rank, combo) for a grid of n_combo x n_rank work-groups:
 // when n_combo is a multiple of 8, each XCD takes its own n_combo/8 combos
 // and, within the XCD, work-groups start in rank order (rank 0 first);
