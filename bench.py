@@ -180,12 +180,22 @@ def sample_sclk(fn, ms_per_call, max_s=10.0):
     exe = "/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else shutil.which("amd-smi")
     if not exe:
         return None
+    cmd = [exe]
+    try:
+        # amd-smi is a Python script: run it with this interpreter, so that no
+        # launcher (`env` in its first line) has to replace itself
+        real = os.path.realpath(exe)
+        with open(real, "rb") as fh:
+            if b"python" in fh.readline():
+                cmd = [sys.executable, real]
+    except OSError:
+        pass
     got = {}
 
     def probe():
         time.sleep(0.5)
         try:
-            r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True, text=True,
+            r = subprocess.run(cmd + ["metric", "-c", "--json"], capture_output=True, text=True,
                                timeout=20)
             d = json.loads(r.stdout)
             clocks = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
