@@ -723,11 +723,17 @@ struct BwdKV {
   // the next BR/4 lanes D) into the stage's tail.
   static __device__ __forceinline__ void issue(const BwdArgs& a, const State& st, int h, int q0,
                                                char* stage) {
-    if (st.wave == 0 && st.lane < BR / 2) {
-      // rows q0 .. q0+BR-1 lie inside the head's ld_rows-long block
-      const float* src = (st.lane < BR / 4 ? a.nl2 : a.delta) +
-                         ((int64_t)st.b * a.Hq + h) * a.ld_rows + q0 + (st.lane % (BR / 4)) * 4;
-      dma16(src, stage + 2 * TL::BYTES);
+    if (st.wave == 0) {
+      // rows q0 .. q0+BR-1 lie inside the head's ld_rows-long block.  Buffer
+      // loads, not global ones: a global load into LDS is a FLAT instruction,
+      // which may also touch LDS, and after one the compiler waits for every
+      // LDS read (lgkmcnt(0)) where the pipeline needs only the oldest
+      const int64_t row0 = ((int64_t)st.b * a.Hq + h) * a.ld_rows + q0;
+      const uint32_t voff = (uint32_t)(st.lane % (BR / 4)) * 16;
+      if (st.lane < BR / 4)
+        dma16_buf(make_rsrc(a.nl2 + row0, BR * 4), voff, stage + 2 * TL::BYTES);
+      else if (st.lane < BR / 2)
+        dma16_buf(make_rsrc(a.delta + row0, BR * 4), voff, stage + 2 * TL::BYTES);
     }
     const int64_t o = (int64_t)h * st.head_bytes + (int64_t)q0 * st.row_bytes;
     const uint32_t n =
