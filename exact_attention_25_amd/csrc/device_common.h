@@ -82,12 +82,6 @@ __device__ __forceinline__ V8 lds_read16(const char* p) {
   return *(const LDS_AS V8*)(const LDS_AS void*)(p);
 }
 
-// One 16-byte global -> LDS copy per lane.  Lane i of the wave writes the
-// 16 bytes at lds_wave_base + 16 * i; lds_wave_base must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* gsrc, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (LDS_AS void*)lds_wave_base, 16, 0, 0);
-}
-
 // s_waitcnt vmcnt(n) for a wave-uniform n in 0..7 (larger n waits for all):
 // at most n vector-memory operations of this wave, the latest issued, stay
 // outstanding.  expcnt and lgkmcnt are left at their maxima (no wait); the
@@ -114,8 +108,11 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-// Same as dma16, through a buffer resource: the lane's 16 bytes at byte
-// offset voff (zero if out of range) land at lds_wave_base + 16 * lane.
+// One 16-byte global -> LDS copy per lane through a buffer resource: the
+// lane's 16 bytes at byte offset voff (zero if out of range) land at
+// lds_wave_base + 16 * lane; lds_wave_base must be wave-uniform.  (Buffer
+// loads count only in vmcnt; a global load into LDS is a FLAT instruction,
+// after which the compiler waits for every outstanding LDS read.)
 __device__ __forceinline__ void dma16_buf(BufRsrc r, uint32_t voff, char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds_wave_base, 16, voff, 0, 0, 0);
 }
