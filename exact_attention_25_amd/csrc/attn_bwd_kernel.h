@@ -973,9 +973,12 @@ struct BwdKV {
     st.l32 = st.lane & 31;
 
     // block -> (key block, chunk, kv-head, batch); key blocks in increasing
-    // order, i.e. (causal) the ones with the most query rows first
-    int kblk, rest;
-    rank_combo(blockIdx.x, a.B * a.Hkv * a.kv_chunks, kblk, rest);
+    // order over the whole grid, i.e. (causal) the ones with the most query
+    // rows first, and every XCD (each 8th work-group) holds blocks of every
+    // batch, whose key lengths may differ
+    const int n_combo = a.B * a.Hkv * a.kv_chunks;
+    const int kblk = blockIdx.x / n_combo;
+    int rest = blockIdx.x % n_combo;
     const int chunk = rest % a.kv_chunks;
     rest /= a.kv_chunks;
     const int g = rest % a.Hkv;
