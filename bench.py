@@ -166,20 +166,22 @@ def time_graph(fn, steps, warmup, outs):
     return ms
 
 
-def sample_sclk(fn, ms_per_call, max_s=10.0):
-    """Mean engine clock (MHz) over the XCDs while fn() runs back to back.
-
-    amd-smi is read once from a second thread, half a second into a stretch
-    of calls; the calls go in batches of ~20 ms with a synchronisation after
-    each, so the GPU stays loaded until the reading is taken and the queue
-    never runs far ahead.  None if amd-smi is missing or prints no clock."""
+def sample_sclk(fn, ms_per_call, n_samples=3, max_s=15.0):
+    """Engine clock (MHz, mean over the XCDs) read with amd-smi while fn()
+    runs back to back: n_samples readings from a second thread, the first
+    half a second into the calls.  The calls go in batches of ~20 ms with a
+    synchronisation after each, so the GPU stays loaded until the last
+    reading and the queue never runs far ahead.  Returns the list of
+    readings ([] if amd-smi is missing or prints no clock).  The clock moves
+    within milliseconds under power management, so each reading is one
+    sample of it."""
     import shutil
     import subprocess
     import threading
     import torch
     exe = "/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else shutil.which("amd-smi")
     if not exe:
-        return None
+        return []
     cmd = [exe]
     try:
         # amd-smi is a Python script: run it with this interpreter, so that no
@@ -190,20 +192,22 @@ def sample_sclk(fn, ms_per_call, max_s=10.0):
                 cmd = [sys.executable, real]
     except OSError:
         pass
-    got = {}
+    got = []
 
     def probe():
         time.sleep(0.5)
-        try:
-            r = subprocess.run(cmd + ["metric", "-c", "--json"], capture_output=True, text=True,
-                               timeout=20)
-            d = json.loads(r.stdout)
-            clocks = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
-            vals = [float(v["clk"]["value"]) for k, v in clocks.items()
-                    if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
-            got["mhz"] = sum(vals) / len(vals) if vals else None
-        except Exception:
-            got["mhz"] = None
+        for _ in range(n_samples):
+            try:
+                r = subprocess.run(cmd + ["metric", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=20)
+                d = json.loads(r.stdout)
+                clocks = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
+                vals = [float(v["clk"]["value"]) for k, v in clocks.items()
+                        if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                if vals:
+                    got.append(sum(vals) / len(vals))
+            except Exception:
+                return
 
     batch = max(1, int(20.0 / max(ms_per_call, 1e-3)))
     th = threading.Thread(target=probe, daemon=True)
@@ -214,15 +218,18 @@ def sample_sclk(fn, ms_per_call, max_s=10.0):
             fn()
         torch.cuda.synchronize()
     th.join(timeout=1.0)
-    return got.get("mhz")
+    return got
 
 
-def clock_fields(mhz, value, peak) -> dict:
-    """The engine clock under load and the %-of-peak at that clock (the
-    published peaks assume 2400 MHz)."""
-    if not mhz:
+def clock_fields(samples, value, peak) -> dict:
+    """The engine clock under load (median of the readings, and the
+    readings) and the %-of-peak at that clock (the published peaks assume
+    2400 MHz)."""
+    if not samples:
         return {"sclk_mhz_under_load": None}
+    mhz = sorted(samples)[len(samples) // 2]
     return {"sclk_mhz_under_load": round(mhz),
+            "sclk_mhz_samples": [round(v) for v in samples],
             "pct_of_peak_at_measured_clock": round(value / (peak * mhz / 2400.0) * 100, 2)}
 
 
@@ -583,7 +590,7 @@ def main():
         ms, _ = time_calls(fn, args.steps, args.warmup, stream)
 
     pct = call_percentiles(fn, min(args.steps, 50), stream)
-    mhz = None if args.no_clock else sample_sclk(fn, ms)
+    clk = [] if args.no_clock else sample_sclk(fn, ms)
 
     tflops = flops / ms / 1e9
     peak = acc.PEAK_TFLOPS["fp8" if fp8 else w.dtype]
@@ -608,7 +615,7 @@ def main():
                        "key_padding": w.lens is not None, "pass": "decode",
                        **local_config(w)},
             "pct_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS * 100, 2),
-            "sclk_mhz_under_load": round(mhz) if mhz else None,
+            "sclk_mhz_under_load": clock_fields(clk, 1.0, 1.0)["sclk_mhz_under_load"],
             "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": acc.PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / acc.PEAK_HBM_GBS, 4),
@@ -661,7 +668,7 @@ def main():
                    "pass": "fp8 forward" if fp8 else ("backward" if bwd else "forward"),
                    **local_config(w)},
         "pct_of_peak": round(tflops / peak * 100, 2),
-        **clock_fields(mhz, tflops, peak),
+        **clock_fields(clk, tflops, peak),
         "tokens_per_s": round(w.B * w.Nq / ms * 1e3, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
