@@ -292,6 +292,14 @@ def test_workload_causal_gqa_forward(gpu_lib, part):
     assert torch.equal(o[:, :, 0], v[:, :, 0].repeat_interleave(G, dim=1))
 
 
+# The pipelined kernel (8-wave work-groups, more than 16 key tiles) on every
+# row of a mid-size call with ragged Nq / Nk tails, 8 q-heads per kv-head and
+# key lengths that end mid-tile (4 * 64 * 8 = 2048 work-groups).
+def test_forward_pipelined_ragged_gqa_lens(gpu_lib):
+    _full_check(inputs.Workload("pipe_bf16_b4_h64_kv8_n2000_d128", 4, 64, 8, 2000, 2000, 128,
+                                "bf16", 41, lens=(1100, 2000)))
+
+
 # the long-context sweep (B * N = 32768); N = 16384 in two halves of the batch
 SWEEP = [(1024, None), (2048, None), (8192, None), (16384, (0,)), (16384, (1,))]
 
