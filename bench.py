@@ -17,7 +17,9 @@ oracle's backward on one (batch, kv-head) group.
 
 --extras also times the other workloads (the ViT, UNet self/cross, causal
 GQA forward and backward, and the long-context sweep) and adds them to the
-JSON line under "extras".
+JSON line under "extras", with the unfused torch chain (Q K^T, scale,
+softmax, P V) at the B8 H32 N4096 d128 shape timed beside the fused call as
+context.
 
 Workloads with a sliding window, a 2-D neighbourhood or a soft cap (the
 FlexAttention cases, e.g. vit_nbr_bf16_b8_h12_n3136_d64) pass them to the
@@ -454,6 +456,43 @@ def run_extras(device, steps, warmup):
     return out
 
 
+def unfused_chain(device, steps, warmup):
+    """The unfused chain the pages compare against (S = Q K^T, scaled,
+    softmax, S V, each a separate torch op in bf16 with the N x N scores in
+    HBM) at the B8 H32 N4096 d128 shape, beside the fused kernel on the same
+    inputs: context for the pages' fused-over-unfused speed-up, not a
+    target.  K^T is made contiguous once, outside the timed calls (torch's
+    batched bf16 products are not given a transposed right operand)."""
+    import torch
+    from exact_attention_25_amd import accounting as acc
+    from exact_attention_25_amd import binding as bd
+    from exact_attention_25_amd import inputs
+    stream = torch.cuda.current_stream(device)
+    w = inputs.WORKLOADS[DEFAULT_WORKLOAD]
+    _, t = workload_inputs(w, device)
+    q, k, v = t["q"], t["k"], t["v"]
+    kt = k.transpose(-1, -2).contiguous()
+    scale = w.d ** -0.5
+
+    def chain():
+        s = torch.matmul(q, kt)
+        return torch.matmul(torch.softmax(s * scale, dim=-1), v)
+
+    ums, _ = time_calls(chain, steps, warmup, stream)
+    o_u = chain()
+    o_f, _ = bd.attn_fwd(q, k, v)
+    fms, _ = time_calls(lambda: bd.attn_fwd(q, k, v), steps, warmup, stream)
+    torch.cuda.synchronize()
+    diff = float((o_u.float() - o_f.float()).abs().max())
+    fl = acc.fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, False)
+    del kt, o_u
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "unfused_ms": round(ums, 4),
+            "unfused_tflops": round(fl / ums / 1e9, 1), "fused_ms": round(fms, 4),
+            "fused_speedup": round(ums / fms, 2), "max_abs_diff_unfused_vs_fused": diff,
+            "scores_bytes_per_call": 2 * w.B * w.Hq * w.Nq * w.Nk}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -691,6 +730,7 @@ def main():
     if args.extras:
         print("[bench] extras", file=sys.stderr, flush=True)
         rec["extras"] = run_extras(device, max(args.steps // 2, 10), 5)
+        rec["extras"]["unfused_chain"] = unfused_chain(device, 10, 3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, x, backward=bwd, fp8=fp8)
