@@ -3,8 +3,8 @@
 B = 260, H = 128, N = 512, d = 128 in bf16 gives 2.18e9 elements per tensor
 (4.4 GB), so the last heads start more than 2^31 elements (and 2^32 bytes)
 into Q, K, V, O and the gradients.  The forward (non-causal and
-causal, both on the pipelined kernel: 512 keys = 8 tiles) and the causal
-backward run on the whole tensors; the heads at the start, the middle and the
+causal, both on the pipelined kernel: 512 keys = 8 tiles), the split-KV
+decode (K / V as the cache) and the causal backward run on the whole tensors; the heads at the start, the middle and the
 very end are checked against the oracle (each head is its own problem:
 Hq = Hkv), to the same bars as the other parity tests.
 
@@ -81,6 +81,31 @@ def test_forward_past_2_31_elements(gpu_lib, big, causal):
         assert _rel_rms(got - O, O) <= TOL_O_REL_RMS["bf16"]
         assert lerr <= 1e-4 + 1e-6 * float(np.abs(L).max())
     del o, lse
+    torch.cuda.empty_cache()
+
+
+def test_decode_past_2_31_elements(gpu_lib, big):
+    # the 4.4 GB K / V as a decode cache of 512 entries per (batch, head), two
+    # new queries per head (the last two positions, causal): their rows equal
+    # the last two rows of causal attention over the whole sequence
+    import torch
+    from exact_attention_25_amd import binding as bd
+    from oracle import ref_fwd_rows
+    _say(f"[large] decode: 2 queries against a B{B} H{H} {N}-entry d{D} bf16 cache")
+    q2 = big["q"][:, :, N - 2:].contiguous()
+    o, lse = bd.attn_decode(q2, big["k"], big["v"], causal=True)
+    torch.cuda.synchronize()
+    for b, h in HEADS:
+        q, k, v = (_head(big[n], b, h) for n in ("q", "k", "v"))
+        O, L = ref_fwd_rows(q, k, v, 0, 0, np.array([N - 2, N - 1]), causal=True)
+        got = _head(o, b, h)[0, 0]
+        err = np.abs(got - O)
+        lerr = float(np.abs(host(lse[b, h]).astype(np.float64) - L).max())
+        _say(f"[large]   head ({b}, {h}): O max-abs {err.max():.3e}, LSE max-abs {lerr:.3e}")
+        assert np.all(np.isfinite(got))
+        assert err.max() <= TOL_O["bf16"]
+        assert lerr <= 1e-4 + 1e-6 * float(np.abs(L).max())
+    del o, lse, q2
     torch.cuda.empty_cache()
 
 
