@@ -83,7 +83,8 @@ def fwd_kernel_name(w) -> str:
     if span >= 8 * 64:
         nw = 4 if span <= 16 * 64 else 8
         bc = 128 if (D == 64 and nw == 8) else 64
-        return f"attn::fwd_pipe_kernel<{e},{D},{bc},causal={str(w.causal).lower()},NW={nw}>"
+        dk = ",DK=48" if (D == 64 and w.d <= 48) else ""
+        return f"attn::fwd_pipe_kernel<{e},{D},{bc},causal={str(w.causal).lower()},NW={nw}{dk}>"
     return f"attn::fwd_kernel<{e},{D},8,64,causal={str(w.causal).lower()},mask=false>"
 
 

@@ -10,19 +10,28 @@
 
 namespace attn {
 
-template <class E, int D, int BC, int PNW>
-static hipError_t launch_pipe(const FwdArgs& a0, bool causal, hipStream_t st) {
-  using P = FwdPipeKernel<E, D, BC, false, PNW>;
+template <class E, int D, int BC, int PNW, int DK>
+static hipError_t launch_pipe_dk(const FwdArgs& a0, bool causal, hipStream_t st) {
+  using P = FwdPipeKernel<E, D, BC, false, PNW, DK>;
   FwdArgs a = a0;
   a.nqb = (a.Nq + P::ROWS - 1) / P::ROWS;
   a.total_blocks = a.B * a.Hq * a.nqb;
   if (causal)
-    hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC, true, PNW>), dim3(a.total_blocks),
+    hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC, true, PNW, DK>), dim3(a.total_blocks),
                        dim3(PNW * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC, false, PNW>), dim3(a.total_blocks),
+    hipLaunchKernelGGL((fwd_pipe_kernel<E, D, BC, false, PNW, DK>), dim3(a.total_blocks),
                        dim3(PNW * 64), 0, st, a);
   return hipGetLastError();
+}
+
+// d <= 48 at D = 64: the QK^T contraction stops at column 48
+template <class E, int D, int BC, int PNW>
+static hipError_t launch_pipe(const FwdArgs& a, bool causal, hipStream_t st) {
+  if constexpr (D == 64) {
+    if (a.d <= 48) return launch_pipe_dk<E, D, BC, PNW, 48>(a, causal, st);
+  }
+  return launch_pipe_dk<E, D, BC, PNW, D>(a, causal, st);
 }
 
 template <class E, int D, int NW, int BC>

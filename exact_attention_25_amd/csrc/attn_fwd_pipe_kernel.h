@@ -46,8 +46,12 @@
 
 namespace attn {
 
-template <class E, int D, int BC, bool CAUSAL, int NW = 8>
+// DK: the width of the QK^T contraction, D or (D = 64, d <= 48) 48: the
+// k-step over columns 48..63 then multiplies only the zeros past d and is
+// skipped (a quarter of the QK^T products and K reads of a d = 40 call).
+template <class E, int D, int BC, bool CAUSAL, int NW = 8, int DK = D>
 struct FwdPipeKernel {
+  static_assert(DK == D || (D == 64 && DK == 48), "QK^T width");
   static constexpr float TH = 8.0f;                 // rescale threshold, log2 units
   // NW waves per work-group: 8 (one work-group per CU), or 4 for short key
   // ranges, where two independent work-groups per CU overlap one's start
@@ -73,7 +77,7 @@ struct FwdPipeKernel {
   static constexpr int K_IPW = (K_INS + NW - 1) / NW;  // ... per wave
   static constexpr int V_IPW = (V_INS + NW - 1) / NW;
   static constexpr int KB = BC / 32;                   // 32-key blocks per tile
-  static constexpr int KS = D / 16;                    // k-steps of QK^T
+  static constexpr int KS = DK / 16;                   // k-steps of QK^T
   static constexpr int DT = D / 32;                    // 32-wide d tiles of O
   static constexpr int PT = BC / 16;                   // 16-key chunks (PV k-steps)
   static constexpr int NQ = KS * KB;                   // QK^T MFMAs per tile
@@ -430,10 +434,10 @@ struct FwdPipeKernel {
   }
 };
 
-template <class E, int D, int BC, bool CAUSAL, int NW>
+template <class E, int D, int BC, bool CAUSAL, int NW, int DK = D>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pipe_kernel(FwdArgs a) {
-  using K = FwdPipeKernel<E, D, BC, CAUSAL, NW>;
+  using K = FwdPipeKernel<E, D, BC, CAUSAL, NW, DK>;
   __shared__ __attribute__((aligned(1024))) char k0[K::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[K::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[K::K_BYTES];

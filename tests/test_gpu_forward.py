@@ -69,6 +69,9 @@ SMALL = [
     ("fp16_d64_pipe128_causal_lens", 2, 2, 1, 1300, 1300, 64, "fp16", True, (700, 1300), None, "bhnd", None, 1.0),
     ("bf16_d40_pipe128_bnhd_ragged", 1, 3, 3, 150, 1500, 40, "bf16", False, None, None, "bnhd", None, 1.0),
     ("fp16_d64_pipe128_large_logits", 1, 2, 2, 64, 1100, 64, "fp16", False, (1030, 1100), None, "bhnd", None, 3.0),
+    # d <= 48: the QK^T contraction of the pipelined kernel stops at column 48
+    ("fp16_d48_pipe128_lens", 1, 2, 2, 300, 1200, 48, "fp16", False, (1100, 1200), None, "bhnd", None, 1.0),
+    ("bf16_d32_pipe_gqa", 1, 4, 2, 130, 600, 32, "bf16", False, None, None, "bhnd", None, 1.0),
 ]
 
 
@@ -185,6 +188,7 @@ PIPE_CAUSAL = [
     ("pipe_causal_fp16_d64_bnhd", 1, 2, 1, 520, 520, 64, "fp16", None, "bnhd"),
     ("pipe_causal_lens_d96", 2, 2, 2, 900, 900, 96, "bf16", (530, 900), "bhnd"),
     ("pipe_causal_fp16_d128_bnhd", 1, 2, 1, 1000, 1000, 128, "fp16", None, "bnhd"),
+    ("pipe_causal_d48_lens", 1, 2, 1, 1100, 1100, 48, "bf16", (600, 1100), "bhnd"),
 ]
 
 
