@@ -56,6 +56,7 @@ FWD = [
     ("fwd_pipelined_bf16", 2, 4, 2, 300, 900, 128, "bf16", False, (530, 700)),
     ("fwd_pipelined_causal_fp16", 2, 4, 2, 800, 800, 64, "fp16", True, (530, 700)),
     ("fwd_pipelined_128_bf16_d64", 2, 2, 1, 300, 1400, 64, "bf16", False, (1100, 1250)),
+    ("fwd_pipelined_128_fp16_d40", 2, 2, 2, 300, 1400, 40, "fp16", False, (1100, 1250)),
     ("fwd_fp32", 2, 2, 2, 100, 150, 64, "fp32", False, (60, 120)),
 ]
 
